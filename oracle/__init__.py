@@ -1,0 +1,31 @@
+"""CPU oracle for the W8A8 / block-scaled FP8 / SmoothQuant INT8 / MXFP4 hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or link this
+package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it. It shares no code with the HIP library (``fp4_w8a8_quantized_amd``)
+and never imports it; the only module both sides use is ``synthetic`` (seeded input
+generators, which hold none of the method's arithmetic).
+
+Everything here is plain NumPy on the CPU, written from the definitions on three pages:
+
+* [P-FP8FP4]  "FP8 and FP4 inference, SmoothQuant and activation quantization"
+* [P-FP8INT8] "FP8 and INT8 Inference"
+* [P-LOWBIT]  "Low-bit LLM Weights and Activations"
+
+Each function names the section it follows. Floating-point work is done in fp64 unless
+the pages fix the precision: the scale and quotient arithmetic of the quantizers runs in
+IEEE fp32, because the pages' emulation of per-token quantization runs on fp32 tensors
+and an integer (the code) is decided by it.
+
+Pinning status (what each part is checked against lives in ``tests/test_oracle_*.py``):
+
+* formats.py      pinned (page values, exhaustive brute force, torch CPU casts)
+* quant.py        pinned (worked example printed on [P-FP8INT8] §4, brute force, invariants)
+* gemm.py         pinned (brute force, scale-factoring identity, [P-FP8FP4] worked example)
+* smoothquant.py  pinned (closed forms printed on [P-LOWBIT] Try-it 02 and [P-FP8FP4])
+* roofline.py     pinned (numbers printed on [P-FP8FP4] and [P-LOWBIT] §5)
+"""
+
+from . import formats, quant, gemm, smoothquant, roofline  # noqa: F401
+
+__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline"]
