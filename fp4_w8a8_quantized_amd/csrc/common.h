@@ -1,0 +1,81 @@
+// Device-side helpers shared by the gfx950 kernels of the W8A8 library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bf16 halves of a packed 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// Two fp32 -> packed bf16x2, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Four fp32 -> four OCP E4M3FN bytes (v_cvt_pk_fp8_f32: round to nearest even). The
+// hardware returns NaN instead of saturating for |v| >= 464; callers guarantee
+// |v| <= 448 * (1 + 2^-23) (dynamic amax scaling), where both behaviours agree.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Quotient x / s (s > 0) from a per-row reciprocal rcp = 1/s (itself an IEEE division):
+// one product and two FMA corrections, then the sign of x (an exact zero sum would
+// otherwise come out as +0 for x = -0). It equals the IEEE fp32 quotient except where
+// the residual underflows, i.e. only for |x / s| < 2^-11, where every FP8 and INT8 code
+// is a zero of the same sign either way; this is checked exhaustively on the host over
+// all bf16 x and all bf16-derived scales.
+__device__ __forceinline__ float div_by_scale(float x, float s, float rcp) {
+  float q0 = __fmul_rn(x, rcp);
+  float r = __builtin_fmaf(-q0, s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, rcp, q0), x);
+}
+
+// Round to nearest even and clamp to [-127, 127], as a byte.
+__device__ __forceinline__ uint32_t int8_code(float v) {
+  int i = (int)__builtin_rintf(v);       // v_rndne_f32 + v_cvt_i32_f32 (exact integer)
+  i = max(-127, min(127, i));
+  return (uint32_t)(i & 0xFF);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// |x| maximum over the 8 bf16 values of a 16-byte chunk.
+__device__ __forceinline__ float chunk_absmax(u32x4 v) {
+  float m = fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x)));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return m;
+}
+
+// max(amax, 1e-8) / qmax with a NaN amax passed through (all-NaN row).
+__device__ __forceinline__ float amax_scale(float amax, float qmax) {
+  float a = (amax != amax) ? amax : fmaxf(amax, 1e-8f);
+  return a / qmax;                      // IEEE fp32 division
+}
+
+}  // namespace w8a8

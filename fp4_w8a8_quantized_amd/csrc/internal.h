@@ -1,0 +1,35 @@
+// Launchers behind the C ABI. Arguments have been validated by api.cpp; each launcher
+// only enqueues kernels on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w8a8 {
+
+hipError_t launch_quantize_rows(const void* x, int64_t R, int64_t K, int fmt, void* q,
+                                float* scale, hipStream_t st);
+hipError_t launch_quantize_group(const void* x, int64_t M, int64_t K, void* q, float* sx,
+                                 hipStream_t st);
+hipError_t launch_quantize_block(const void* w, int64_t N, int64_t K, void* q, float* sw,
+                                 hipStream_t st);
+hipError_t launch_quantize_mxfp4(const void* x, int64_t R, int64_t K, void* q, uint8_t* sc,
+                                 hipStream_t st);
+
+hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
+                       int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st);
+hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
+                                   const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                   hipStream_t st);
+hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
+                             const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
+                             hipStream_t st);
+
+hipError_t launch_channel_absmax(const void* x, int64_t R, int64_t K, float* amax,
+                                 hipStream_t st);
+hipError_t launch_smooth_scales(const float* a, const float* w, int64_t K, float alpha,
+                                float* s, hipStream_t st);
+hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float* s, int mode,
+                               void* out, hipStream_t st);
+
+}  // namespace w8a8

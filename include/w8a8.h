@@ -1,0 +1,173 @@
+/*
+ * w8a8.h - C ABI of the MI355X (gfx950) W8A8 / block-scaled FP8 / INT8 / MXFP4 library.
+ *
+ * The calls follow the problem statement of three pages:
+ *   [P-FP8FP4]  "FP8 and FP4 inference, SmoothQuant and activation quantization"
+ *   [P-FP8INT8] "FP8 and INT8 Inference"
+ *   [P-LOWBIT]  "Low-bit LLM Weights and Activations"
+ * A quantized linear layer computes Y = X W^T as diag(s_X) (X_q W_q^T) diag(s_W): the
+ * operands are quantized to 8-bit (or 4-bit) codes with one scale per token (row of X)
+ * and one per output channel (row of W), the contraction runs in low precision with
+ * FP32 (INT32 for INT8) accumulation, and the scales are applied after the reduction
+ * ([P-FP8FP4] "Scale granularity"; [P-LOWBIT] §3.4).
+ *
+ * Conventions shared by every call:
+ *  - Layouts are row-major. X is [M, K] (tokens x in-features), W is [N, K] (out x in,
+ *    the layout of a PyTorch Linear weight), Y is [M, N]. K is contiguous in X and W.
+ *  - bf16 means IEEE bfloat16 bit patterns (2 bytes); E4M3FN means OCP FP8 E4M3FN
+ *    bytes (max 448, NaN 0x7F/0xFF); E2M1 codes are packed two per byte, element 2i in
+ *    the low nibble; E8M0 scales are bytes whose value is 2^(c - 127).
+ *  - Array arguments are device pointers that the caller allocated and owns, except
+ *    where a comment says "host". The library keeps no pointer after a call returns,
+ *    allocates no memory, holds no mutable global state and is re-entrant.
+ *  - Device pointers must be 16-byte aligned. Inputs and outputs must not overlap.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream. Calls are
+ *    asynchronous: they enqueue kernels and return; outputs are valid once the stream
+ *    has synchronized.
+ *  - Every argument check runs on the host before anything is enqueued. On a non-zero
+ *    status nothing has been enqueued and no output has been written.
+ *  - A dimension of 0 rows (M, N or R) is valid and enqueues nothing.
+ *  - Non-finite inputs are outside the contract: the kernels do not fault on them, a
+ *    NaN element encodes to a NaN code, and a scale computed from an infinite amax is
+ *    infinite.
+ */
+#ifndef W8A8_H
+#define W8A8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W8A8_OK = 0,
+  W8A8_ERR_NULL = 1,        /* a required pointer is NULL                              */
+  W8A8_ERR_SHAPE = 2,       /* a dimension is negative, or a size overflows int64      */
+  W8A8_ERR_UNSUPPORTED = 3, /* K is not a multiple of the call's granule, bad format   */
+  W8A8_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned                 */
+  W8A8_ERR_HIP = 5,         /* the HIP runtime reported an error when enqueuing        */
+  W8A8_ERR_ARG = 6          /* a scalar argument is out of range (e.g. alpha, mode)    */
+} w8a8_status;
+
+typedef enum {
+  W8A8_FMT_E4M3FN = 0,      /* OCP FP8 E4M3FN codes, FP32 accumulation                 */
+  W8A8_FMT_INT8 = 1         /* symmetric INT8 codes in [-127, 127], INT32 accumulation */
+} w8a8_format;
+
+/* Human-readable name of a status code (static string; never NULL). */
+const char* w8a8_status_string(int status);
+
+/* ------------------------------------------------------------------------------------
+ * Per-token dynamic activation quantization ([P-FP8FP4] "Implementation sketch",
+ * fp8_per_token; [P-FP8INT8] §5 "INT8 in practice": activations per-token, dynamic).
+ *
+ * For each row m of x_bf16 [M, K]:
+ *   amax = max_k |x[m,k]|
+ *   E4M3FN: s[m] = fp32(max(amax, 1e-8)) / 448   q[m,k] = e4m3_rne_sat(x[m,k] / s[m])
+ *   INT8:   s[m] = fp32(max(amax, 1e-8)) / 127   q[m,k] = clamp(rne(x[m,k] / s[m]), +-127)
+ * Both divisions are IEEE fp32 divisions rounded to nearest even; the E4M3FN encode
+ * rounds to nearest even and saturates to +-448 (0x7E / 0xFE); zeros keep their sign.
+ *   q:     [M, K] bytes (E4M3FN codes or int8)      scale: fp32 [M]
+ * K must be a multiple of 16. Returns W8A8_ERR_UNSUPPORTED otherwise.
+ */
+w8a8_status w8a8_quantize_per_token(const void* x_bf16, int64_t M, int64_t K, int fmt,
+                                    void* q, float* scale, void* stream);
+
+/* Per-output-channel weight quantization: exactly the per-token rule applied to the
+ * rows of w_bf16 [N, K] (one scale per output channel; [P-FP8FP4] "Scale granularity",
+ * [P-FP8INT8] §5: weights per-channel, static). Done once, offline.
+ *   q: [N, K] bytes    scale: fp32 [N]    K % 16 == 0. */
+w8a8_status w8a8_quantize_weight_per_channel(const void* w_bf16, int64_t N, int64_t K, int fmt,
+                                             void* q, float* scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * W8A8 GEMM with the fused scale epilogue ([P-FP8INT8] §5 and the epilogue of §6-9;
+ * [P-LOWBIT] §3.4 and §4.3):
+ *   E4M3FN: y[m,n] = bf16_rne( s_x[m] * s_w[n] * sum_k dec(xq[m,k]) * dec(wq[n,k]) ),
+ *           products and sums in FP32 (the summation order is unspecified).
+ *   INT8:   acc = sum_k xq[m,k] * wq[n,k] exactly in INT32;
+ *           y[m,n] = bf16_rne( fp32( fp32(acc) * s_x[m] ) * s_w[n] ), bit-exact.
+ *   xq [M, K], wq [N, K] codes; sx fp32 [M]; sw fp32 [N]; y_bf16 [M, N].
+ * K must be a multiple of 128 (W8A8_ERR_UNSUPPORTED otherwise); K = 0 is not allowed.
+ */
+w8a8_status w8a8_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
+                      int64_t M, int64_t N, int64_t K, int fmt, void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * DeepSeek-V3-style fine-grained FP8 ([P-FP8INT8] §5 "What DeepSeek did" and "The
+ * blockwise/fine-grained trend"; [P-FP8FP4] "Scale granularity").
+ *
+ * 1x128 activation groups: each run of 128 elements along K gets its own scale,
+ *   sx[m, g] = fp32(max(amax_{m,g}, 1e-8)) / 448, codes as in w8a8_quantize_per_token.
+ *   xq: [M, K] E4M3FN    sx: fp32 [M, K/128] (row-major)    K % 128 == 0.
+ */
+w8a8_status w8a8_quantize_per_token_group(const void* x_bf16, int64_t M, int64_t K,
+                                          void* xq, float* sx, void* stream);
+
+/* 128x128 weight blocks: one scale per (block of 128 output rows, block of 128 K).
+ *   wq: [N, K] E4M3FN    sw: fp32 [ceil(N/128), K/128]    K % 128 == 0.
+ * The last row block is partial when N % 128 != 0. */
+w8a8_status w8a8_quantize_weight_block(const void* w_bf16, int64_t N, int64_t K,
+                                       void* wq, float* sw, void* stream);
+
+/* Block-scaled FP8 GEMM with FP32 promotion once per 128-wide K group:
+ *   y[m,n] = bf16_rne( sum_g sx[m,g] * sw[n/128, g] * (sum_{k in g} dec(xq) dec(wq)) ),
+ * the inner sum in FP32 from zero for each group, the outer running sum in FP32.
+ * K % 128 == 0. */
+w8a8_status w8a8_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
+                                  const float* sw, int64_t M, int64_t N, int64_t K,
+                                  void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * MXFP4 ([P-LOWBIT] §2.4: E2M1 elements, one E8M0 power-of-two scale per 32 elements,
+ * 4.25 bits per weight; [P-FP8FP4] "Where it came from").
+ *
+ * Quantize the rows of any bf16 [R, K] matrix (activations or weights), per 32-element
+ * block along K: amax of the block; e = floor(log2(amax)) - 2 clamped to [-127, 127]
+ * (0 for an all-zero block); scale code e + 127; elements x / 2^e rounded to E2M1 with
+ * round-to-nearest-even and saturation to +-6.
+ *   q_packed: [R, K/2] bytes    scale_e8m0: [R, K/32] bytes    K % 32 == 0.
+ */
+w8a8_status w8a8_quantize_mxfp4(const void* x_bf16, int64_t R, int64_t K, void* q_packed,
+                                uint8_t* scale_e8m0, void* stream);
+
+/* MXFP4 x MXFP4 GEMM on the gfx950 block-scaled matrix cores:
+ *   y[m,n] = bf16_rne( sum_b 2^(ex[m,b]-127) 2^(ew[n,b]-127) sum_{k in b} dec(xq) dec(wq) ),
+ *   accumulated in FP32. xq [M, K/2], wq [N, K/2] packed; sx [M, K/32]; sw [N, K/32].
+ * K % 256 == 0. */
+w8a8_status w8a8_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
+                            const uint8_t* sw, int64_t M, int64_t N, int64_t K,
+                            void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * SmoothQuant preparation for the INT8 variant ([P-FP8FP4] "SmoothQuant: move the
+ * outliers into the weights" and the `smooth` emulation; [P-LOWBIT] §4.2-4.3). Offline.
+ *
+ * Column maxima of a bf16 [R, K] matrix: amax[j] = max_r |x[r, j]| (exact); for a
+ * calibration batch this is max|X_:j|, for W [N, K] it is max|W_:j| over output rows.
+ *   amax: fp32 [K]    K % 8 == 0. R = 0 writes zeros.
+ */
+w8a8_status w8a8_channel_absmax(const void* x_bf16, int64_t R, int64_t K, float* amax,
+                                void* stream);
+
+/* Smoothing factors s[j] = max(act_max[j], 1e-5)^alpha / max(w_max[j], 1e-5)^(1-alpha),
+ * evaluated in fp32. alpha = 0.5 uses correctly rounded square roots and one correctly
+ * rounded division (a fully specified fp32 result); alpha = 0 and 1 reduce to 1/w and a;
+ * other alpha in (0, 1) use exp2/log2 and are accurate to a few ulp.
+ *   act_max, w_max, s: fp32 [K] device arrays.    0 <= alpha <= 1 (W8A8_ERR_ARG). */
+w8a8_status w8a8_smoothquant_scales(const float* act_max, const float* w_max, int64_t K,
+                                    float alpha, float* s, void* stream);
+
+/* Apply smoothing to a bf16 [R, K] matrix, column j by s[j]:
+ *   mode 0 (activations): out = bf16_rne(fp32(x) / s[j])   (IEEE fp32 division)
+ *   mode 1 (weights):     out = bf16_rne(fp32(x) * s[j])
+ * out_bf16: [R, K]    K % 8 == 0; other modes return W8A8_ERR_ARG. */
+w8a8_status w8a8_smooth_apply(const void* x_bf16, int64_t R, int64_t K, const float* s,
+                              int mode, void* out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H */

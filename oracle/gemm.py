@@ -59,7 +59,21 @@ def gemm_fp8_bruteforce(xq, sx, wq, sw) -> np.ndarray:
 
 
 def gemm_int8_acc(xq, wq) -> np.ndarray:
-    """Exact INT32 accumulator acc[m,n] = sum_k xq[m,k] * wq[n,k] (computed in int64)."""
+    """Exact INT32 accumulator acc[m,n] = sum_k xq[m,k] * wq[n,k].
+
+    Computed as an fp64 matrix product of the integer codes: every product and every
+    partial sum is an integer of magnitude at most K * 127^2, below 2^53 for any K under
+    5e11, so the fp64 sums are exact in any order and the result converts back exactly.
+    """
+    xq = np.asarray(xq)
+    wq = np.asarray(wq)
+    if xq.shape[-1] * 127 * 127 >= 2 ** 53:
+        raise ValueError("K too large for an exact fp64 integer product")
+    return (xq.astype(np.float64) @ wq.astype(np.float64).T).astype(np.int64)
+
+
+def gemm_int8_acc_bruteforce(xq, wq) -> np.ndarray:
+    """Same accumulator with int64 arithmetic only (slow; for pins on small shapes)."""
     return np.asarray(xq, np.int64) @ np.asarray(wq, np.int64).T
 
 

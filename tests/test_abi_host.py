@@ -1,0 +1,123 @@
+"""C-ABI host tests (no GPU): the library loads, exports every call declared in
+include/w8a8.h, and rejects bad arguments on the host before enqueuing anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w8a8.h")
+
+import fp4_w8a8_quantized_amd as w8  # noqa: E402
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EHIP, EARG = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(w8.library_path):
+        pytest.fail("libw8a8.so is not built (run __graft_entry__.build())")
+    return w8.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:w8a8_status|const char\*)\s+(w8a8_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["w8a8_quantize_per_token", "w8a8_quantize_weight_per_channel", "w8a8_gemm",
+              "w8a8_quantize_per_token_group", "w8a8_quantize_weight_block", "w8a8_gemm_blockscaled",
+              "w8a8_quantize_mxfp4", "w8a8_gemm_mxfp4", "w8a8_channel_absmax",
+              "w8a8_smoothquant_scales", "w8a8_smooth_apply", "w8a8_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(declared_functions()) - {"w8a8_status_string"} == set(w8._SIGNATURES)
+
+
+def test_status_strings(L):
+    assert w8.status_string(OK) == "ok"
+    for s in range(1, 7):
+        assert w8.status_string(s) not in ("ok", "unknown status")
+    assert w8.status_string(99) == "unknown status"
+
+
+# Fake, never-dereferenced addresses: validation must fail before any launch.
+A = 0x10000          # 16-byte aligned
+MIS = 0x10008        # 8-byte aligned only
+
+
+def test_quantize_validation(L):
+    q = L.w8a8_quantize_per_token
+    assert q(None, 4, 128, 0, A, A, None) == ENULL
+    assert q(A, 4, 128, 0, None, A, None) == ENULL
+    assert q(A, 4, 128, 0, A, None, None) == ENULL
+    assert q(A, -1, 128, 0, A, A, None) == ESHAPE
+    assert q(A, 4, -16, 0, A, A, None) == ESHAPE
+    assert q(A, 4, 100, 0, A, A, None) == EUNSUP          # K % 16 != 0
+    assert q(A, 4, 128, 7, A, A, None) == EUNSUP          # unknown format
+    assert q(MIS, 4, 128, 0, A, A, None) == EALIGN
+    assert q(A, 4, 128, 1, A, MIS, None) == EALIGN
+    assert q(A, 1 << 40, 1 << 20, 0, A, A, None) == ESHAPE
+    assert q(None, 0, 128, 0, None, None, None) == OK     # empty: nothing to do
+    w = L.w8a8_quantize_weight_per_channel
+    assert w(None, 4, 128, 0, A, A, None) == ENULL
+    assert w(A, 4, 40, 1, A, A, None) == EUNSUP
+
+
+def test_gemm_validation(L):
+    g = L.w8a8_gemm
+    assert g(None, A, A, A, 4, 4, 128, 0, A, None) == ENULL
+    assert g(A, A, A, A, 4, 4, 128, 0, None, None) == ENULL
+    assert g(A, A, A, A, 4, 4, 100, 0, A, None) == EUNSUP   # K % 128
+    assert g(A, A, A, A, 4, 4, 0, 0, A, None) == EUNSUP     # K == 0
+    assert g(A, A, A, A, 4, 4, 128, 3, A, None) == EUNSUP   # format
+    assert g(A, A, A, A, -4, 4, 128, 0, A, None) == ESHAPE
+    assert g(A, A, A, A, 4, 1 << 40, 128, 0, A, None) == ESHAPE
+    assert g(A, A, MIS, A, 4, 4, 128, 0, A, None) == EALIGN
+    assert g(A, A, A, A, 4, 4, 128, 0, MIS, None) == EALIGN
+    assert g(None, None, None, None, 0, 4, 128, 0, None, None) == OK
+    assert g(None, None, None, None, 4, 0, 128, 1, None, None) == OK
+
+
+def test_blockscaled_validation(L):
+    assert L.w8a8_quantize_per_token_group(A, 4, 100, A, A, None) == EUNSUP
+    assert L.w8a8_quantize_per_token_group(None, 4, 128, A, A, None) == ENULL
+    assert L.w8a8_quantize_weight_block(A, 4, 192, A, A, None) == EUNSUP
+    assert L.w8a8_quantize_weight_block(A, 4, 256, A, MIS, None) == EALIGN
+    assert L.w8a8_gemm_blockscaled(A, A, A, A, 4, 4, 64, A, None) == EUNSUP
+    assert L.w8a8_gemm_blockscaled(A, None, A, A, 4, 4, 128, A, None) == ENULL
+
+
+def test_mxfp4_validation(L):
+    assert L.w8a8_quantize_mxfp4(A, 4, 48, A, A, None) == EUNSUP
+    assert L.w8a8_quantize_mxfp4(A, 4, 64, None, A, None) == ENULL
+    assert L.w8a8_gemm_mxfp4(A, A, A, A, 4, 4, 128, A, None) == EUNSUP   # K % 256
+    assert L.w8a8_gemm_mxfp4(A, A, A, A, 4, 4, 256, None, None) == ENULL
+    assert L.w8a8_gemm_mxfp4(A, MIS, A, A, 4, 4, 256, A, None) == EALIGN
+
+
+def test_smoothquant_validation(L):
+    assert L.w8a8_smoothquant_scales(A, A, 8, ctypes.c_float(1.5), A, None) == EARG
+    assert L.w8a8_smoothquant_scales(A, A, 8, ctypes.c_float(-0.1), A, None) == EARG
+    assert L.w8a8_smoothquant_scales(A, A, 8, ctypes.c_float(float("nan")), A, None) == EARG
+    assert L.w8a8_smoothquant_scales(None, A, 8, ctypes.c_float(0.5), A, None) == ENULL
+    assert L.w8a8_smooth_apply(A, 4, 8, A, 2, A, None) == EARG
+    assert L.w8a8_smooth_apply(A, 4, 12, A, 0, A, None) == EUNSUP
+    assert L.w8a8_smooth_apply(A, 4, 8, None, 0, A, None) == ENULL
+    assert L.w8a8_channel_absmax(A, 4, 12, A, None) == EUNSUP
+    assert L.w8a8_channel_absmax(A, 4, 8, None, None) == ENULL
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros((4, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w8.quantize_per_token(x)

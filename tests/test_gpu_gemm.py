@@ -1,0 +1,243 @@
+"""GPU parity: the HIP GEMMs (FP8, INT8 + SmoothQuant, block-scaled FP8, MXFP4) against the
+oracle. Codes, scales and INT8 outputs bit for bit; FP8 / FP4 outputs within
+|y - y_ref| <= 1e-2 (|y_ref| + rms(y_ref)) of the oracle's fp64 contraction."""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+import fp4_w8a8_quantized_amd as w8
+from oracle import gemm as G
+from oracle import quant as Q
+from oracle import smoothquant as S
+from tests.gpu_util import (bf16_bits, bf16_to_f64, bits_i8, bits_u8, f32, first_mismatch,
+                            need_gpu, to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _bf16(v):
+    return synthetic.to_bf16_bits(np.asarray(v, np.float64))
+
+
+def _assert_tol(y_gpu, y_ref, what):
+    ok, worst = G.within_tolerance(y_gpu, y_ref, TOL)
+    assert ok, f"{what}: worst error / bound = {worst:.3f}"
+
+
+def _xw(M, N, K, seed, outliers=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K))
+    if outliers:
+        ch = rng.choice(K, size=max(1, K // 1000), replace=False)
+        x[:, ch] *= rng.uniform(50, 500, size=len(ch))
+    w = rng.standard_normal((N, K)) * 0.02
+    return _bf16(x), _bf16(w)
+
+
+# ----------------------------------------------------------------------------- FP8
+def _fp8_full_compare(xb, wb, what):
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    xq, sx = w8.quantize_per_token(x)
+    wq, sw = w8.quantize_weight_per_channel(w)
+    y = w8.gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    oxq, osx = Q.quantize_per_token_fp8(xb)
+    owq, osw = Q.quantize_weight_per_channel_fp8(wb)
+    assert np.array_equal(bits_u8(xq), oxq) and np.array_equal(f32(sx), osx)
+    assert np.array_equal(bits_u8(wq), owq) and np.array_equal(f32(sw), osw)
+    _assert_tol(bf16_to_f64(y), G.gemm_fp8_ref(oxq, osx, owq, osw), what)
+
+
+def test_fp8_tiny_config():
+    need_gpu()
+    x, w = synthetic.tiny()
+    _fp8_full_compare(x, w, "tiny 16x128x256")
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 256), (3, 1000, 4096),
+                                   (256, 256, 128), (513, 129, 1024), (260, 4100, 256)])
+def test_fp8_ragged(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, M * 31 + N * 7 + K)
+    _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3])
+def test_fp8_prefill_full_size_sampled(i):
+    """The 8B prefill linears at full size, in the bench's launch configuration; codes of
+    sampled rows are compared exactly and a sampled output block within tolerance."""
+    need_gpu()
+    name, xb, wb = synthetic.prefill(i)
+    M, K = xb.shape
+    N = wb.shape[0]
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    xq, sx = w8.quantize_per_token(x)
+    wq, sw = w8.quantize_weight_per_channel(w)
+    y = w8.gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + i)
+    rows = np.sort(np.concatenate([[0, M - 1], rng.choice(M, 62, replace=False)]))
+    cols = np.sort(np.concatenate([[0, N - 1], rng.choice(N, 254, replace=False)]))
+    oxq, osx = Q.quantize_per_token_fp8(xb[rows])
+    owq, osw = Q.quantize_weight_per_channel_fp8(wb[cols])
+    gxq = bits_u8(xq[torch.as_tensor(rows, device="cuda:0")])
+    gwq = bits_u8(wq[torch.as_tensor(cols, device="cuda:0")])
+    assert np.array_equal(gxq, oxq), first_mismatch(gxq, oxq)
+    assert np.array_equal(gwq, owq), first_mismatch(gwq, owq)
+    assert np.array_equal(f32(sx)[rows], osx) and np.array_equal(f32(sw)[cols], osw)
+    yg = bf16_to_f64(y)[np.ix_(rows, cols)]
+    _assert_tol(yg, G.gemm_fp8_ref(oxq, osx, owq, osw), f"prefill {name}")
+
+
+@pytest.mark.parametrize("N", synthetic.DECODE_NS)
+def test_fp8_decode_sweep(N):
+    need_gpu()
+    xall = synthetic.decode_x()
+    wb = synthetic.decode_w(N)
+    w = to_dev_bf16(wb)
+    wq, sw = w8.quantize_weight_per_channel(w)
+    owq, osw = Q.quantize_weight_per_channel_fp8(wb)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_u8(wq), owq) and np.array_equal(f32(sw), osw)
+    for M in synthetic.DECODE_MS:
+        xb = xall[:M]
+        xq, sx = w8.quantize_per_token(to_dev_bf16(xb))
+        y = w8.gemm(xq, sx, wq, sw)
+        torch.cuda.synchronize()
+        oxq, osx = Q.quantize_per_token_fp8(xb)
+        assert np.array_equal(bits_u8(xq), oxq)
+        _assert_tol(bf16_to_f64(y), G.gemm_fp8_ref(oxq, osx, owq, osw), f"decode M={M} N={N}")
+
+
+# ----------------------------------------------------------------------------- INT8
+def _int8_chain(xb, xcal, wb, alpha, what):
+    """SmoothQuant + INT8 W8A8 on both sides, every stage compared bit for bit."""
+    x, xc, w = to_dev_bf16(xb), to_dev_bf16(xcal), to_dev_bf16(wb)
+    ax = w8.channel_absmax(xc)
+    aw = w8.channel_absmax(w)
+    s = w8.smoothquant_scales(ax, aw, alpha)
+    xh = w8.smooth_apply(x, s, "activation")
+    wh = w8.smooth_apply(w, s, "weight")
+    xq, sx = w8.quantize_per_token(xh, "int8")
+    wq, sw = w8.quantize_weight_per_channel(wh, "int8")
+    y = w8.gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    oax, oaw = S.channel_absmax(xcal), S.channel_absmax(wb)
+    assert np.array_equal(f32(ax), oax) and np.array_equal(f32(aw), oaw)
+    os_ = S.smooth_scales(oax, oaw, alpha)
+    assert np.array_equal(f32(s).view(np.uint32), os_.view(np.uint32)), first_mismatch(f32(s), os_)
+    oxh, owh = S.smooth_activations(xb, os_), S.smooth_weights(wb, os_)
+    assert np.array_equal(bf16_bits(xh), oxh), first_mismatch(bf16_bits(xh), oxh)
+    assert np.array_equal(bf16_bits(wh), owh), first_mismatch(bf16_bits(wh), owh)
+    oxq, osx = Q.quantize_per_token_int8(oxh)
+    owq, osw = Q.quantize_weight_per_channel_int8(owh)
+    assert np.array_equal(bits_i8(xq), oxq) and np.array_equal(f32(sx), osx)
+    assert np.array_equal(bits_i8(wq), owq) and np.array_equal(f32(sw), osw)
+    oy = G.gemm_int8_ref(oxq, osx, owq, osw)
+    gy = bf16_bits(y)
+    assert np.array_equal(gy, oy), f"{what}: " + first_mismatch(gy, oy)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 1024), (64, 256, 14336)])
+def test_int8_ragged(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, M + N + K)
+    xcal, _ = _xw(64, 1, K, K)
+    _int8_chain(xb, xcal, wb, 0.5, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("N", synthetic.DECODE_NS)
+def test_int8_smoothquant_decode_sweep(N):
+    need_gpu()
+    xall = synthetic.decode_x()
+    xcal = synthetic.decode_calibration()
+    wb = synthetic.decode_w(N)
+    for M in synthetic.DECODE_MS:
+        _int8_chain(xall[:M], xcal, wb, 0.5, f"decode M={M} N={N}")
+
+
+def test_smoothquant_general_alpha():
+    need_gpu()
+    xcal, wb = _xw(64, 96, 256, 5)
+    ax, aw = w8.channel_absmax(to_dev_bf16(xcal)), w8.channel_absmax(to_dev_bf16(wb))
+    for alpha in (0.0, 0.25, 0.85, 1.0):
+        s = f32(w8.smoothquant_scales(ax, aw, alpha))
+        os_ = S.smooth_scales(S.channel_absmax(xcal), S.channel_absmax(wb), alpha)
+        if alpha in (0.0, 1.0):
+            assert np.array_equal(s, os_)
+        else:
+            np.testing.assert_allclose(s, os_, rtol=2e-6)
+
+
+# ----------------------------------------------------------------------------- block-scaled
+def _block_compare(xb, wb, what, rows=None, wblocks=None):
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    xq, sx = w8.quantize_per_token_group(x)
+    wq, sw = w8.quantize_weight_block(w)
+    y = w8.gemm_blockscaled(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    M, N = xb.shape[0], wb.shape[0]
+    rows = np.arange(M) if rows is None else rows
+    cols = np.arange(N) if wblocks is None else np.concatenate(
+        [np.arange(b * 128, min(N, (b + 1) * 128)) for b in wblocks])
+    oxq, osx = Q.quantize_per_token_group_fp8(xb[rows])
+    owq, osw = Q.quantize_weight_block_fp8(wb[cols])
+    assert np.array_equal(bits_u8(xq)[rows], oxq) and np.array_equal(f32(sx)[rows], osx)
+    assert np.array_equal(bits_u8(wq)[cols], owq)
+    gsw = f32(sw)[np.arange(N)[cols][::128] // 128]
+    assert np.array_equal(gsw, osw)
+    _assert_tol(bf16_to_f64(y)[np.ix_(rows, cols)], G.gemm_blockscaled_ref(oxq, osx, owq, osw), what)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 1024), (64, 256, 7168)])
+def test_blockscaled_ragged(M, N, K):
+    need_gpu()
+    rng = np.random.default_rng(M * 3 + N + K)
+    xb = _bf16(rng.standard_t(3, size=(M, K)))
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02)
+    _block_compare(xb, wb, f"{M}x{N}x{K}")
+
+
+def test_blockscaled_full_size_sampled():
+    need_gpu()
+    xb, wb = synthetic.blockscaled()
+    rng = np.random.default_rng(44)
+    rows = np.sort(np.concatenate([[0, xb.shape[0] - 1], rng.choice(xb.shape[0], 62, replace=False)]))
+    _block_compare(xb, wb, "block-scaled 4096x18432x7168", rows=rows, wblocks=[0, 77, 143])
+
+
+# ----------------------------------------------------------------------------- MXFP4
+def _mx_compare(xb, wb, what, rows=None, cols=None):
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    xq, sx = w8.quantize_mxfp4(x)
+    wq, sw = w8.quantize_mxfp4(w)
+    y = w8.gemm_mxfp4(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    rows = np.arange(xb.shape[0]) if rows is None else rows
+    cols = np.arange(wb.shape[0]) if cols is None else cols
+    oxq, osx = Q.quantize_mxfp4(xb[rows])
+    owq, osw = Q.quantize_mxfp4(wb[cols])
+    assert np.array_equal(bits_u8(xq)[rows], oxq) and np.array_equal(bits_u8(sx)[rows], osx)
+    assert np.array_equal(bits_u8(wq)[cols], owq) and np.array_equal(bits_u8(sw)[cols], osw)
+    _assert_tol(bf16_to_f64(y)[np.ix_(rows, cols)], G.gemm_mxfp4_ref(oxq, osx, owq, osw), what)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 256), (17, 130, 512), (300, 549, 1024), (64, 256, 8192)])
+def test_mxfp4_ragged(M, N, K):
+    need_gpu()
+    xb = synthetic.mxfp4_x(M, K)
+    wb = _bf16(np.random.default_rng(N + K).standard_normal((N, K)) * 0.02)
+    _mx_compare(xb, wb, f"{M}x{N}x{K}")
+
+
+def test_mxfp4_full_size_sampled():
+    need_gpu()
+    xb, wb = synthetic.mxfp4()
+    rng = np.random.default_rng(55)
+    rows = np.sort(np.concatenate([[0, 8191], rng.choice(8192, 62, replace=False)]))
+    cols = np.sort(np.concatenate([[0, 8191], rng.choice(8192, 190, replace=False)]))
+    _mx_compare(xb, wb, "mxfp4 8192^3", rows=rows, cols=cols)

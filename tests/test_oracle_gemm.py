@@ -66,7 +66,9 @@ def test_int8_acc_exact_and_epilogue_order():
     xq = rng.integers(-127, 128, (7, 14336)).astype(np.int8)
     wq = rng.integers(-127, 128, (9, 14336)).astype(np.int8)
     acc = G.gemm_int8_acc(xq, wq)
-    assert np.array_equal(acc, (xq.astype(np.float64) @ wq.astype(np.float64).T).astype(np.int64))
+    assert np.array_equal(acc, G.gemm_int8_acc_bruteforce(xq, wq))
+    big = np.full((1, 14336), 127, np.int8)
+    assert G.gemm_int8_acc(big, -big)[0, 0] == -14336 * 127 * 127
     acc_loop = np.array([[sum(int(a) * int(b) for a, b in zip(xq[m], wq[n])) for n in range(2)] for m in range(2)])
     assert np.array_equal(acc[:2, :2], acc_loop)
     # epilogue: fp32(fp32(acc) * s_x) * s_w, each product rounded, then bf16 RNE
