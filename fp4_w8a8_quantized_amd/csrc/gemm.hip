@@ -1,29 +1,35 @@
 // Low-precision GEMMs with fused scale epilogues on gfx950 matrix cores.
 //
 //   FP8    y = bf16( s_x[m] s_w[n] sum_k dec(xq) dec(wq) )      v_mfma_f32_16x16x128_f8f6f4
-//   INT8   y = bf16( fp32(fp32(acc_i32) s_x[m]) s_w[n] )        v_mfma_i32_16x16x64_i8
-//   BLOCK  y = bf16( sum_g s_x[m,g] s_w[n/128,g] partial_g )    fp32 partial per 128-K group
-//   MXFP4  y = bf16( sum_b 2^ex 2^ew sum dec4 dec4 )            v_mfma_scale_f32_16x16x128_f8f6f4
+//   BLOCK  y = bf16( sum_g s_x[m,g] s_w[n/128,g] partial_g )    same, one fp32 partial per 128-K group
+//   INT8   y = bf16( fp32(fp32(acc_i32) s_x[m]) s_w[n] )        v_mfma_i32_32x32x32_i8
+//   MXFP4  y = bf16( sum_b 2^ex 2^ew sum dec4 dec4 )            v_mfma_scale_f32_32x32x64_f8f6f4
 //
 // The scales are applied after the low-precision reduction, which the scale-factoring
 // identity diag(s_X)(X_q W_q^T)diag(s_W) allows ("FP8 and FP4 inference, SmoothQuant and
-// activation quantization", Scale granularity; "FP8 and INT8 Inference" §6-9 epilogue;
-// "Low-bit LLM Weights and Activations" §3.4). The block-scaled variant promotes each
-// 128-wide K group's fp32 partial into the running fp32 sum ("FP8 and INT8 Inference" §5,
-// What DeepSeek did); MXFP4 lets the matrix core apply the E8M0 block scales
-// ("Low-bit LLM Weights and Activations" §2.4).
+// activation quantization", Scale granularity; "FP8 and INT8 Inference" §6-9, the GEMM
+// epilogue; "Low-bit LLM Weights and Activations" §3.4). The block-scaled variant
+// promotes each 128-wide K group's fp32 partial into the running fp32 sum ("FP8 and INT8
+// Inference" §5, What DeepSeek did); MXFP4 lets the matrix core apply the E8M0 block
+// scales ("Low-bit LLM Weights and Activations" §2.4). INT8 and FP4 use the 32x32 MFMA
+// shapes, which run at twice the rate of their 16x16 forms on gfx950.
 //
-// Structure (one 256-thread workgroup = 4 waves per output tile of 256 x BN):
-//  - K advances 128 bytes per step (128 FP8/INT8 or 256 FP4 elements); X [256 x 128 B]
-//    and W [BN x 128 B] stage through a double-buffered LDS tile (global -> VGPR -> LDS),
-//    the next step's global loads in flight while the current step runs on the MFMAs.
-//  - LDS rows are 128 B; 16-byte chunk c of row r sits at chunk slot c ^ (r & 7), so the
-//    fragment reads (16 rows x 32 B per instruction) are bank-conflict free.
-//  - The waves form a 2 x 2 grid: each owns 128 rows of X and BN/2 rows of W. The MFMA
-//    A operand is a W fragment and B an X fragment, so each lane's four accumulators are
-//    four consecutive output columns of one row: the epilogue stores 8 contiguous bytes.
-//  - Workgroup ids are remapped so that consecutive tiles land on the same XCD (ids are
-//    dealt round-robin over the 8 XCDs) and tiles sharing a W panel share an L2.
+// One 256-thread workgroup (4 waves, 2 x 2) computes a 256 x BN output tile:
+//  - K advances 128 bytes per step (128 FP8/INT8 elements, 256 FP4 elements). The X
+//    [256 x 128 B] and W [BN x 128 B] slices of a step land in an LDS stage by direct
+//    global->LDS loads (no register staging). STAGES buffers give the loads STAGES-1
+//    steps to land.
+//  - LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), which
+//    keeps fragment reads free of bank conflicts on the 64-bank LDS.
+//  - Fragments are double-buffered in registers: while step k's MFMAs run, the wave reads
+//    step k+1's fragments, so MFMAs never wait on LDS after a step boundary. One barrier
+//    per step publishes the next stage and retires the one just read.
+//  - The A operand of every MFMA is a W fragment and B an X fragment, so each lane's
+//    accumulators are runs of four consecutive output columns of one row.
+//  - The epilogue scales and converts in registers, stages the bf16 tile through the
+//    now-free LDS, and writes whole rows with 16-byte stores.
+//  - Workgroup ids are remapped so that consecutive tiles (which share a W panel) land
+//    on the same XCD and its L2 (ids are dealt round-robin over the 8 XCDs).
 #include <type_traits>
 
 #include "common.h"
@@ -36,210 +42,296 @@ enum Kind : int { KIND_FP8 = 0, KIND_INT8 = 1, KIND_BLOCK = 2, KIND_MXFP4 = 3 };
 constexpr int kBM = 256;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+// Byte offset of chunk `chunk` of LDS tile row `row`.
+__device__ __forceinline__ int tile_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
-template <int BN, int KIND>
+// One 16-byte direct global->LDS load per lane: lane l writes LDS bytes
+// [lds_addr + 16 l, +16) (M0 holds the wave's LDS address) from gbase + voff. Issued as
+// inline assembly so that the compiler does not serialize it against unrelated LDS reads;
+// completion is tracked by hand with vmcnt waits before the barrier that publishes a stage.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, uint32_t voff, const uint8_t* gbase) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory");
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Makes a register value opaque at this point of the instruction stream. Placed right
+// after a step's barrier, it pins the compiler's wait for a scale load to a moment when
+// no direct-to-LDS load is in flight (vmcnt retires in issue order, so a later wait on an
+// earlier scale load would also wait for every DMA issued after it).
+template <class T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
+template <int BN, int KIND, int STAGES>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
             const uint8_t* __restrict__ wq, const void* __restrict__ swp, int M, int N,
             int Kb, int ksteps, uint16_t* __restrict__ y, int tiles_m, int vec_store) {
-  constexpr int SM = 8;                 // 16-row X subtiles per wave (128 rows)
-  constexpr int SN = BN / 32;           // 16-row W subtiles per wave (BN/2 rows)
-  constexpr int XCH = kBM / 32;         // 16-byte X chunks per thread per step
-  constexpr int WCH = BN / 32;          // 16-byte W chunks per thread per step
-  constexpr int XT = kBM * 128, WT = BN * 128;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (XT + WT)];
+  constexpr bool MF32 = (KIND == KIND_INT8 || KIND == KIND_MXFP4);
+  constexpr int SUB = MF32 ? 32 : 16;         // MFMA output tile edge
+  constexpr int SM = 128 / SUB;               // X subtiles per wave (128 rows)
+  constexpr int SN = (BN / 2) / SUB;          // W subtiles per wave (BN/2 rows)
+  static_assert(SN * SUB * 2 == BN, "tile width must split into whole subtiles");
+  constexpr int XT = kBM * 128, WT = BN * 128, STAGE = XT + WT;
+  constexpr int XI = kBM / 32, WI = BN / 32;  // 1 KB DMA instructions per wave per step
+  constexpr int DMA_PER_STEP = XI + WI;
+  constexpr int FR = MF32 ? 16 : 8;           // fragment registers per subtile
+  typedef int frag_t __attribute__((ext_vector_type(FR)));
+  typedef typename std::conditional<KIND == KIND_INT8, int, float>::type acc_e;
+  typedef acc_e acc_t __attribute__((ext_vector_type(MF32 ? 16 : 4)));
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave & 1, wn = wave >> 1;
-
   int b = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
   const int tm = b % tiles_m, tn = b / tiles_m;
   const int m0 = tm * kBM, n0 = tn * BN;
 
-  // Global -> LDS staging map: thread t moves chunk (t & 7) of rows (t >> 3) + 32 i.
-  const int lrow = t >> 3, lch = t & 7;
-  uint32_t xo[XCH], wo[WCH];
+  // DMA map: instruction i of wave w fills tile rows 8q..8q+7 (q = w + 4 i); lane l
+  // writes slot (l & 7) of row 8q + (l >> 3), which holds chunk (l & 7) ^ ((row >> 1) & 7).
+  // Rows past M or N re-read the last valid row (their results are never stored).
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+  uint32_t xoff[XI], woff[WI];
 #pragma unroll
-  for (int i = 0; i < XCH; ++i) xo[i] = (uint32_t)min(m0 + lrow + 32 * i, M - 1) * (uint32_t)Kb + lch * 16;
+  for (int i = 0; i < XI; ++i) {
+    const int r = 8 * (wave + 4 * i) + (lane >> 3);
+    xoff[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)Kb + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
 #pragma unroll
-  for (int i = 0; i < WCH; ++i) wo[i] = (uint32_t)min(n0 + lrow + 32 * i, N - 1) * (uint32_t)Kb + lch * 16;
-  const int st_off = lds_off(lrow, lch);   // row lrow + 32 i has the same (row & 7)
+  for (int i = 0; i < WI; ++i) {
+    const int r = 8 * (wave + 4 * i) + (lane >> 3);
+    woff[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)Kb + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
+  auto dma = [&](int ks, int stage) {
+    const uint8_t* xb = xq + (size_t)ks * 128;
+    const uint8_t* wb = wq + (size_t)ks * 128;
+    const uint32_t sbase = lds0 + stage * STAGE + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < XI; ++i) lds_dma16(sbase + i * 4096, xoff[i], xb);
+#pragma unroll
+    for (int i = 0; i < WI; ++i) lds_dma16(sbase + XT + i * 4096, woff[i], wb);
+  };
 
-  // Fragment map: lane reads row (lane & 15) of a 16-row subtile, chunks 2g and 2g + 1.
-  const int fr = lane & 15, g = lane >> 4;
-  const int fo0 = fr * 128 + (((2 * g) ^ (fr & 7)) << 4);
-  const int fo1 = fr * 128 + (((2 * g + 1) ^ (fr & 7)) << 4);
+  // Fragment map. 16x16x128: lane reads row (lane & 15), chunks 2g, 2g+1 (g = lane >> 4).
+  // 32x32: lane reads row (lane & 31), chunks h, h+2, h+4, h+6 (h = lane >> 5); chunk
+  // 2q + h feeds the q-th of the four 32/64-deep MFMAs of the step.
+  const int fr = MF32 ? (lane & 31) : (lane & 15);
+  const int g = MF32 ? (lane >> 5) : (lane >> 4);
+  int fo[FR / 4];
+#pragma unroll
+  for (int c = 0; c < FR / 4; ++c) fo[c] = tile_off(fr, MF32 ? (2 * c + g) : (2 * g + c));
   const int xrow0 = wm * 128, wrow0 = wn * (BN / 2);
+  auto frag = [&](const uint8_t* base) -> frag_t {
+    frag_t f;
+#pragma unroll
+    for (int c = 0; c < FR / 4; ++c) {
+      const i32x4 v = *reinterpret_cast<const i32x4*>(base + fo[c]);
+      f[4 * c + 0] = v[0]; f[4 * c + 1] = v[1]; f[4 * c + 2] = v[2]; f[4 * c + 3] = v[3];
+    }
+    return f;
+  };
 
-  typedef typename std::conditional<KIND == KIND_INT8, i32x4, f32x4>::type acc_t;
   acc_t acc[SN][SM];
 #pragma unroll
   for (int j = 0; j < SN; ++j)
 #pragma unroll
-    for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{0, 0, 0, 0};
+    for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{};
 
-  // Per-lane scale state of the block-scaled and MXFP4 variants.
-  const int G = ksteps;                    // one scale column per K step
-  int srow[SM];
+  // Scale state (block-scaled: fp32 per row group and W block; MXFP4: E8M0 bytes).
+  const int G = ksteps;
+  int srow[SM], swrow[SN];
 #pragma unroll
-  for (int i = 0; i < SM; ++i) srow[i] = min(m0 + xrow0 + 16 * i + fr, M - 1);
-  int swrow[SN];
+  for (int i = 0; i < SM; ++i) srow[i] = min(m0 + xrow0 + SUB * i + fr, M - 1);
 #pragma unroll
-  for (int j = 0; j < SN; ++j) swrow[j] = min(n0 + wrow0 + 16 * j + fr, N - 1);
-
-  u32x4 xs[XCH], ws[WCH];
-  auto gload = [&](int ks) {
-    const uint32_t kof = (uint32_t)ks * 128u;
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) xs[i] = *reinterpret_cast<const u32x4*>(xq + xo[i] + kof);
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) ws[i] = *reinterpret_cast<const u32x4*>(wq + wo[i] + kof);
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* X = lds + buf * (XT + WT);
-    uint8_t* W = X + XT;
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) *reinterpret_cast<u32x4*>(X + st_off + i * 4096) = xs[i];
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) *reinterpret_cast<u32x4*>(W + st_off + i * 4096) = ws[i];
-  };
-  auto frag = [&](const uint8_t* base) -> i32x8 {
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + fo0);
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + fo1);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < ksteps) gload(ks + 1);
-
-    // scales for this K step (block-scaled: fp32 per row group / W block; MXFP4: the two
-    // E8M0 bytes of this lane's blocks 2g and 2g + 1)
-    float sxv[SM], swv[SN];
-    uint32_t sxe[SM], swe[SN];
-    if (KIND == KIND_BLOCK) {
+  for (int j = 0; j < SN; ++j) swrow[j] = min(n0 + wrow0 + SUB * j + fr, N - 1);
+  float bsx[SM], bsw[SN];            // block-scaled: scales of the step being computed
+  u32x2 esx[SM], esw[SN];            // MXFP4: the 8 E8M0 bytes of the step being computed
+  auto load_scales = [&](int ks, float (&fx)[SM], float (&fw)[SN], u32x2 (&ex)[SM], u32x2 (&ew)[SN]) {
+    if constexpr (KIND == KIND_BLOCK) {
       const float* sx = reinterpret_cast<const float*>(sxp);
       const float* sw = reinterpret_cast<const float*>(swp);
 #pragma unroll
-      for (int i = 0; i < SM; ++i) sxv[i] = sx[(size_t)srow[i] * G + ks];
-#pragma unroll
-      for (int j = 0; j < SN; ++j) swv[j] = sw[(size_t)(min(n0 + wrow0 + 16 * j, N - 1) >> 7) * G + ks];
-    }
-    if (KIND == KIND_MXFP4) {
-      const uint8_t* sx = reinterpret_cast<const uint8_t*>(sxp);
-      const uint8_t* sw = reinterpret_cast<const uint8_t*>(swp);
-      const int S = ksteps * 8;            // E8M0 bytes per row
-#pragma unroll
-      for (int i = 0; i < SM; ++i)
-        sxe[i] = *reinterpret_cast<const uint16_t*>(sx + (size_t)srow[i] * S + ks * 8 + 2 * g);
+      for (int i = 0; i < SM; ++i) fx[i] = sx[(size_t)srow[i] * G + ks];
 #pragma unroll
       for (int j = 0; j < SN; ++j)
-        swe[j] = *reinterpret_cast<const uint16_t*>(sw + (size_t)swrow[j] * S + ks * 8 + 2 * g);
+        fw[j] = sw[(size_t)(min(n0 + wrow0 + SUB * j, N - 1) >> 7) * G + ks];
     }
+    if constexpr (KIND == KIND_MXFP4) {
+      const uint8_t* sx = reinterpret_cast<const uint8_t*>(sxp);
+      const uint8_t* sw = reinterpret_cast<const uint8_t*>(swp);
+      const int S = ksteps * 8;
+#pragma unroll
+      for (int i = 0; i < SM; ++i) ex[i] = *reinterpret_cast<const u32x2*>(sx + (size_t)srow[i] * S + ks * 8);
+#pragma unroll
+      for (int j = 0; j < SN; ++j) ew[j] = *reinterpret_cast<const u32x2*>(sw + (size_t)swrow[j] * S + ks * 8);
+    }
+  };
 
-    const uint8_t* X = lds + cur * (XT + WT);
+  // ---- prologue: stages 0..STAGES-1 in flight, stage 0 published, F(0) in registers
+  frag_t xf[SM], wf0[SN], wf1[SN];
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s) dma(min(s, ksteps - 1), s);
+  load_scales(0, bsx, bsw, esx, esw);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 1) * DMA_PER_STEP, 15));
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < SM; ++i) xf[i] = frag(lds + (xrow0 + SUB * i) * 128);
+#pragma unroll
+  for (int j = 0; j < SN; ++j) wf0[j] = frag(lds + XT + (wrow0 + SUB * j) * 128);
+
+  // ---- one K step. Branch-free: near the end the DMA re-fetches the last step into the
+  // stage just retired and the next-fragment reads see a stale stage; neither is used.
+  auto step = [&](int ks, frag_t (&wcur)[SN], frag_t (&wnxt)[SN]) {
+    // Own loads of step ks+1 landed (later steps may still be in flight), own fragment
+    // reads of step ks done; then the barrier makes stage ks+1 visible to every wave and
+    // guarantees that stage ks (read during the previous step) is free.
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 2) * DMA_PER_STEP, 0));
+    lds_barrier();
+    if constexpr (KIND == KIND_BLOCK) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i) pin(bsx[i]);
+#pragma unroll
+      for (int j = 0; j < SN; ++j) pin(bsw[j]);
+    }
+    if constexpr (KIND == KIND_MXFP4) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i) pin(esx[i]);
+#pragma unroll
+      for (int j = 0; j < SN; ++j) pin(esw[j]);
+    }
+    float nsx[SM], nsw[SN];
+    u32x2 nex[SM], new_[SN];
+    load_scales(min(ks + 1, ksteps - 1), nsx, nsw, nex, new_);
+    dma(min(ks + STAGES, ksteps - 1), ks % STAGES);
+    const uint8_t* X = lds + ((ks + 1) % STAGES) * STAGE;
     const uint8_t* W = X + XT;
-    i32x8 xf[SM];
-#pragma unroll
-    for (int i = 0; i < SM; ++i) xf[i] = frag(X + (xrow0 + 16 * i) * 128);
-#pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const i32x8 wf = frag(W + (wrow0 + 16 * j) * 128);
-#pragma unroll
-      for (int i = 0; i < SM; ++i) {
-        if constexpr (KIND == KIND_FP8) {
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
-        } else if constexpr (KIND == KIND_INT8) {
-          const i32x4 wl = __builtin_shufflevector(wf, wf, 0, 1, 2, 3);
-          const i32x4 wh = __builtin_shufflevector(wf, wf, 4, 5, 6, 7);
-          const i32x4 xl = __builtin_shufflevector(xf[i], xf[i], 0, 1, 2, 3);
-          const i32x4 xh = __builtin_shufflevector(xf[i], xf[i], 4, 5, 6, 7);
-          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, xl, acc[j][i], 0, 0, 0);
-          acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, xh, acc[j][i], 0, 0, 0);
-        } else if constexpr (KIND == KIND_BLOCK) {
-          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf, xf[i], zero, 0, 0, 0, 0, 0, 0);
-          const float sc = sxv[i] * swv[j];
-          acc[j][i] += p * sc;
-        } else {
-          // FP4 operands use the low 16 bytes of each fragment register group.
-          const i32x8 wf2 = __builtin_shufflevector(wf, wf, 4, 5, 6, 7, 0, 1, 2, 3);
-          const i32x8 xf2 = __builtin_shufflevector(xf[i], xf[i], 4, 5, 6, 7, 0, 1, 2, 3);
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf, xf[i], acc[j][i], 4, 4, 0, (int)(swe[j] & 0xFFu), 0, (int)(sxe[i] & 0xFFu));
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              wf2, xf2, acc[j][i], 4, 4, 0, (int)(swe[j] >> 8), 0, (int)(sxe[i] >> 8));
-        }
-      }
-    }
-
-    if (ks + 1 < ksteps) sstore(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: lane holds rows m = m0 + xrow0 + 16 i + (lane & 15), columns
-  // n = n0 + wrow0 + 16 j + 4 (lane >> 4) + {0..3}.
-  const float* sxf = reinterpret_cast<const float*>(sxp);
-  const float* swf = reinterpret_cast<const float*>(swp);
-#pragma unroll
-  for (int j = 0; j < SN; ++j) {
-    const int n = n0 + wrow0 + 16 * j + 4 * g;
-    float swr[4] = {1.f, 1.f, 1.f, 1.f};
-    if (KIND == KIND_FP8 || KIND == KIND_INT8) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) swr[r] = swf[min(n + r, N - 1)];
-    }
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
-      const int m = m0 + xrow0 + 16 * i + fr;
-      if (m >= M) continue;
-      float v[4];
-      if constexpr (KIND == KIND_FP8) {
-        const float sm = sxf[m];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[j][i][r] * (sm * swr[r]);
-      } else if constexpr (KIND == KIND_INT8) {
-        const float sm = sxf[m];
+      for (int j = 0; j < SN; ++j) {
+        if constexpr (KIND == KIND_FP8) {
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+        } else if constexpr (KIND == KIND_BLOCK) {
+          const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          acc[j][i] += p * (bsx[i] * bsw[j]);
+        } else if constexpr (KIND == KIND_INT8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = __fmul_rn(__fmul_rn((float)acc[j][i][r], sm), swr[r]);
-      } else {
+          for (int q = 0; q < 4; ++q) {
+            const i32x4 a = {wcur[j][4 * q], wcur[j][4 * q + 1], wcur[j][4 * q + 2], wcur[j][4 * q + 3]};
+            const i32x4 bb = {xf[i][4 * q], xf[i][4 * q + 1], xf[i][4 * q + 2], xf[i][4 * q + 3]};
+            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bb, acc[j][i], 0, 0, 0);
+          }
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[j][i][r];
+          for (int q = 0; q < 4; ++q) {
+            // FP4 operands occupy the low 16 bytes of the operand registers. The lane's
+            // 32 elements form block 2q + h of the step, whose scale byte it supplies.
+            const i32x8 a = {wcur[j][4 * q], wcur[j][4 * q + 1], wcur[j][4 * q + 2], wcur[j][4 * q + 3], 0, 0, 0, 0};
+            const i32x8 bb = {xf[i][4 * q], xf[i][4 * q + 1], xf[i][4 * q + 2], xf[i][4 * q + 3], 0, 0, 0, 0};
+            const int blk = 2 * q + g;
+            const int ea = (int)((((blk < 4) ? esw[j].x : esw[j].y) >> (8 * (blk & 3))) & 0xFFu);
+            const int eb = (int)((((blk < 4) ? esx[i].x : esx[i].y) >> (8 * (blk & 3))) & 0xFFu);
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[j][i], 4, 4, 0, ea, 0, eb);
+          }
+        }
       }
-      uint16_t* yr = y + (size_t)m * N;
-      if (vec_store && n + 3 < N) {
-        u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(yr + n) = o;
-      } else {
+      xf[i] = frag(X + (xrow0 + SUB * i) * 128);
+      if (i < SN) wnxt[i] = frag(W + (wrow0 + SUB * i) * 128);
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) yr[n + r] = (uint16_t)(pack_bf16x2(v[r], 0.f) & 0xFFFFu);
+    for (int j = SM; j < SN; ++j) wnxt[j] = frag(W + (wrow0 + SUB * j) * 128);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) { bsx[i] = nsx[i]; esx[i] = nex[i]; }
+#pragma unroll
+    for (int j = 0; j < SN; ++j) { bsw[j] = nsw[j]; esw[j] = new_[j]; }
+  };
+  int ks = 0;
+  for (; ks + 1 < ksteps; ks += 2) {
+    step(ks, wf0, wf1);
+    step(ks + 1, wf1, wf0);
+  }
+  if (ks < ksteps) step(ks, wf0, wf1);
+
+  // ---- epilogue: scale + convert in registers, stage the bf16 tile through LDS (free
+  // once every in-flight load has landed and every wave left the loop), then write whole
+  // rows with 16-byte stores. Row stride is padded by 16 B (conflict-free 8-byte writes
+  // down a column); at BN = 256 the padding does not fit, so chunks are XOR-swizzled.
+  constexpr int RS = BN == 256 ? 512 : BN * 2 + 16;
+  static_assert(kBM * RS <= STAGES * STAGE, "output tile must fit in the pipeline LDS");
+  auto opos = [&](int row, int byte) -> int {
+    return BN == 256 ? row * RS + ((((byte >> 4) ^ (row & 15)) << 4) | (byte & 15)) : row * RS + byte;
+  };
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+  lds_barrier();
+  const float* sxf = reinterpret_cast<const float*>(sxp);
+  const float* swf = reinterpret_cast<const float*>(swp);
+  constexpr int NG = MF32 ? 4 : 1;            // runs of 4 columns per lane per subtile
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int rl = xrow0 + SUB * i + fr;
+    float sm = 1.f;
+    if (KIND == KIND_FP8 || KIND == KIND_INT8) sm = sxf[min(m0 + rl, M - 1)];
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        const int cl = wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const acc_e a = acc[j][i][4 * q + r];
+          if constexpr (KIND == KIND_FP8) {
+            v[r] = a * (sm * swf[min(n0 + cl + r, N - 1)]);
+          } else if constexpr (KIND == KIND_INT8) {
+            v[r] = __fmul_rn(__fmul_rn((float)a, sm), swf[min(n0 + cl + r, N - 1)]);
+          } else {
+            v[r] = a;
+          }
+        }
+        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
       }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  lds_barrier();
+  constexpr int CPR = BN / 8;                 // 16-byte chunks per output row
+  for (int c = t; c < kBM * CPR; c += kThreads) {
+    const int rl = c / CPR, ch = c - rl * CPR;
+    const int m = m0 + rl, n = n0 + ch * 8;
+    if (m >= M || n >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + opos(rl, ch * 16));
+    uint16_t* yr = y + (size_t)m * N;
+    if (vec_store && n + 7 < N) {
+      *reinterpret_cast<u32x4*>(yr + n) = v;
+    } else {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) yr[n + e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     }
   }
 }
 
-// Tile width along N: among the widths a kernel variant supports, the one that fills the
-// 256 CUs with the fewest workgroup waves (work per wave grows with BN); ties go to the
-// wider tile. The block-scaled variant keeps a second fp32 partial per accumulator and
-// the MXFP4 variant two scale registers per subtile, so they stop at narrower tiles to
-// stay within the register file without spilling.
-static int pick_bn(int64_t M, int64_t N, int max_bn) {
-  const int cands[4] = {256, 224, 192, 128};
+// Tile width along N: among the widths a variant supports, the one that fills the 256
+// CUs with the fewest workgroup waves (work per wave grows with BN); ties go wider.
+static int pick_bn(int64_t M, int64_t N, const int* cands, int nc) {
   const int64_t tm = (M + kBM - 1) / kBM;
-  int best = 128;
+  int best = cands[nc - 1];
   int64_t best_cost = INT64_MAX;
-  for (int c : cands) {
-    if (c > max_bn) continue;
+  for (int i = 0; i < nc; ++i) {
+    const int c = cands[i];
     const int64_t tiles = tm * ((N + c - 1) / c);
     const int64_t cost = ((tiles + 255) / 256) * c;
     if (cost < best_cost) { best_cost = cost; best = c; }
@@ -247,52 +339,62 @@ static int pick_bn(int64_t M, int64_t N, int max_bn) {
   return best;
 }
 
-template <int BN, int KIND>
-static void launch_bn(dim3 grid, hipStream_t st, const void* xq, const void* sx, const void* wq,
-                      const void* sw, int64_t M, int64_t N, int64_t Kb, int ksteps, void* y,
-                      int tiles_m, int vec) {
-  hipLaunchKernelGGL((gemm_kernel<BN, KIND>), grid, dim3(kThreads), 0, st, (const uint8_t*)xq,
-                     sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)Kb, ksteps, (uint16_t*)y,
-                     tiles_m, vec);
-}
-
-template <int KIND>
-static hipError_t launch_kind(const void* xq, const void* sx, const void* wq, const void* sw,
-                              int64_t M, int64_t N, int64_t Kb, void* y, hipStream_t st) {
-  constexpr int kMaxBN = KIND == KIND_BLOCK ? 128 : (KIND == KIND_MXFP4 ? 224 : 256);
-  const int bn = pick_bn(M, N, kMaxBN);
+template <int BN, int KIND, int STAGES>
+static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, const void* wq,
+                            const void* sw, int64_t M, int64_t N, int64_t Kb, void* y) {
   const int tiles_m = (int)((M + kBM - 1) / kBM);
-  const int tiles_n = (int)((N + bn - 1) / bn);
+  const int tiles_n = (int)((N + BN - 1) / BN);
   const int ksteps = (int)(Kb / 128);
-  const int vec = (N % 4) == 0;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
-  if constexpr (kMaxBN >= 256) {
-    if (bn == 256) { launch_bn<256, KIND>(grid, st, xq, sx, wq, sw, M, N, Kb, ksteps, y, tiles_m, vec); return hipGetLastError(); }
-  }
-  if constexpr (kMaxBN >= 224) {
-    if (bn == 224) { launch_bn<224, KIND>(grid, st, xq, sx, wq, sw, M, N, Kb, ksteps, y, tiles_m, vec); return hipGetLastError(); }
-    if (bn == 192) { launch_bn<192, KIND>(grid, st, xq, sx, wq, sw, M, N, Kb, ksteps, y, tiles_m, vec); return hipGetLastError(); }
-  }
-  launch_bn<128, KIND>(grid, st, xq, sx, wq, sw, M, N, Kb, ksteps, y, tiles_m, vec);
+  const int vec = (N % 8) == 0;
+  hipLaunchKernelGGL((gemm_kernel<BN, KIND, STAGES>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kThreads), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
+                     (int)M, (int)N, (int)Kb, ksteps, (uint16_t*)y, tiles_m, vec);
   return hipGetLastError();
 }
 
+// Tile widths per variant. 16x16 variants: 256, 224, 192 (two LDS stages) and 128
+// (three stages: deeper prefetch fits in LDS). 32x32 variants need multiples of 64. The
+// block-scaled variant keeps a per-group partial and its scales in registers, so it
+// stops at 192; the scale-carrying variants use two stages so that one vmcnt(0) per step
+// also retires their scale loads.
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st) {
-  if (fmt == 1) return launch_kind<KIND_INT8>(xq, sx, wq, sw, M, N, K, y, st);
-  return launch_kind<KIND_FP8>(xq, sx, wq, sw, M, N, K, y, st);
+  if (fmt == 1) {
+    static const int c[3] = {256, 192, 128};
+    switch (pick_bn(M, N, c, 3)) {
+      case 256: return launch_bn<256, KIND_INT8, 2>(st, xq, sx, wq, sw, M, N, K, y);
+      case 192: return launch_bn<192, KIND_INT8, 2>(st, xq, sx, wq, sw, M, N, K, y);
+      default: return launch_bn<128, KIND_INT8, 3>(st, xq, sx, wq, sw, M, N, K, y);
+    }
+  }
+  static const int c[4] = {256, 224, 192, 128};
+  switch (pick_bn(M, N, c, 4)) {
+    case 256: return launch_bn<256, KIND_FP8, 2>(st, xq, sx, wq, sw, M, N, K, y);
+    case 224: return launch_bn<224, KIND_FP8, 2>(st, xq, sx, wq, sw, M, N, K, y);
+    case 192: return launch_bn<192, KIND_FP8, 2>(st, xq, sx, wq, sw, M, N, K, y);
+    default: return launch_bn<128, KIND_FP8, 3>(st, xq, sx, wq, sw, M, N, K, y);
+  }
 }
 
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                    hipStream_t st) {
-  return launch_kind<KIND_BLOCK>(xq, sx, wq, sw, M, N, K, y, st);
+  static const int c[2] = {192, 128};
+  switch (pick_bn(M, N, c, 2)) {
+    case 192: return launch_bn<192, KIND_BLOCK, 2>(st, xq, sx, wq, sw, M, N, K, y);
+    default: return launch_bn<128, KIND_BLOCK, 2>(st, xq, sx, wq, sw, M, N, K, y);
+  }
 }
 
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
                              const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t st) {
-  return launch_kind<KIND_MXFP4>(xq, sx, wq, sw, M, N, K / 2, y, st);
+  static const int c[3] = {256, 192, 128};
+  switch (pick_bn(M, N, c, 3)) {
+    case 256: return launch_bn<256, KIND_MXFP4, 2>(st, xq, sx, wq, sw, M, N, K / 2, y);
+    case 192: return launch_bn<192, KIND_MXFP4, 2>(st, xq, sx, wq, sw, M, N, K / 2, y);
+    default: return launch_bn<128, KIND_MXFP4, 2>(st, xq, sx, wq, sw, M, N, K / 2, y);
+  }
 }
 
 }  // namespace w8a8
