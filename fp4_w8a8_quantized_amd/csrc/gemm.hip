@@ -51,8 +51,10 @@ __device__ __forceinline__ int tile_off(int row, int chunk) {
 // [lds_addr + 16 l, +16) (M0 holds the wave's LDS address) from gbase + voff. Issued as
 // inline assembly so that the compiler does not serialize it against unrelated LDS reads;
 // completion is tracked by hand with vmcnt waits before the barrier that publishes a stage.
+// gfx9 wants one wait state between an SALU write of M0 and an LDS-DMA that reads it; the
+// compiler cannot see inside the asm to insert it, so the s_nop does.
 __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, uint32_t voff, const uint8_t* gbase) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory");
 }
 
@@ -113,15 +115,19 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     const int r = 8 * (wave + 4 * i) + (lane >> 3);
     woff[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)Kb + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
-  auto dma = [&](int ks, int stage) {
+  // DMA instructions [first, first + count) of a step, X rows first, then W rows.
+  auto dma_part = [&](int ks, int stage, int first, int count) {
     const uint8_t* xb = xq + (size_t)ks * 128;
     const uint8_t* wb = wq + (size_t)ks * 128;
     const uint32_t sbase = lds0 + stage * STAGE + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < XI; ++i) lds_dma16(sbase + i * 4096, xoff[i], xb);
+    for (int i = 0; i < XI; ++i)
+      if (i >= first && i < first + count) lds_dma16(sbase + i * 4096, xoff[i], xb);
 #pragma unroll
-    for (int i = 0; i < WI; ++i) lds_dma16(sbase + XT + i * 4096, woff[i], wb);
+    for (int i = 0; i < WI; ++i)
+      if (XI + i >= first && XI + i < first + count) lds_dma16(sbase + XT + i * 4096, woff[i], wb);
   };
+  auto dma = [&](int ks, int stage) { dma_part(ks, stage, 0, DMA_PER_STEP); };
 
   // Fragment map. 16x16x128: lane reads row (lane & 15), chunks 2g, 2g+1 (g = lane >> 4).
   // 32x32: lane reads row (lane & 31), chunks h, h+2, h+4, h+6 (h = lane >> 5); chunk
@@ -190,8 +196,13 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
   for (int j = 0; j < SN; ++j) wf0[j] = frag(lds + XT + (wrow0 + SUB * j) * 128);
 
-  // ---- one K step. Branch-free: near the end the DMA re-fetches the last step into the
+  // ---- one K step, branch-free: near the end the loads re-fetch the last step into the
   // stage just retired and the next-fragment reads see a stale stage; neither is used.
+  // The loads of step ks+STAGES go out in groups between the MFMA rows of the first half
+  // of the step, so the CU's address unit (about 1 KB per 16 cycles, shared by the four
+  // waves) works behind the matrix cores instead of holding back their issue.
+  constexpr int DMA_SLOTS = SM / 2;
+  constexpr int DPS = (DMA_PER_STEP + DMA_SLOTS - 1) / DMA_SLOTS;
   auto step = [&](int ks, frag_t (&wcur)[SN], frag_t (&wnxt)[SN]) {
     // Own loads of step ks+1 landed (later steps may still be in flight), own fragment
     // reads of step ks done; then the barrier makes stage ks+1 visible to every wave and
@@ -213,7 +224,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     float nsx[SM], nsw[SN];
     u32x2 nex[SM], new_[SN];
     load_scales(min(ks + 1, ksteps - 1), nsx, nsw, nex, new_);
-    dma(min(ks + STAGES, ksteps - 1), ks % STAGES);
+    const int kdma = min(ks + STAGES, ksteps - 1);
     const uint8_t* X = lds + ((ks + 1) % STAGES) * STAGE;
     const uint8_t* W = X + XT;
 #pragma unroll
@@ -248,6 +259,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
       }
       xf[i] = frag(X + (xrow0 + SUB * i) * 128);
       if (i < SN) wnxt[i] = frag(W + (wrow0 + SUB * i) * 128);
+      if (i < DMA_SLOTS) dma_part(kdma, ks % STAGES, i * DPS, DPS);
     }
 #pragma unroll
     for (int j = SM; j < SN; ++j) wnxt[j] = frag(W + (wrow0 + SUB * j) * 128);
@@ -272,16 +284,29 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   auto opos = [&](int row, int byte) -> int {
     return BN == 256 ? row * RS + ((((byte >> 4) ^ (row & 15)) << 4) | (byte & 15)) : row * RS + byte;
   };
+  // The per-row and per-column scales this lane needs are loaded in one batch, so their
+  // latencies overlap, before the first epilogue barrier.
+  constexpr int NG = MF32 ? 4 : 1;            // runs of 4 columns per lane per subtile
+  constexpr bool SCALED = (KIND == KIND_FP8 || KIND == KIND_INT8);
+  float esm[SM], esn[SN][NG][4];
+  if constexpr (SCALED) {
+    const float* sxf = reinterpret_cast<const float*>(sxp);
+    const float* swf = reinterpret_cast<const float*>(swp);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) esm[i] = sxf[min(m0 + xrow0 + SUB * i + fr, M - 1)];
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int q = 0; q < NG; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          esn[j][q][r] = swf[min(n0 + wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g) + r, N - 1)];
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   lds_barrier();
-  const float* sxf = reinterpret_cast<const float*>(sxp);
-  const float* swf = reinterpret_cast<const float*>(swp);
-  constexpr int NG = MF32 ? 4 : 1;            // runs of 4 columns per lane per subtile
 #pragma unroll
   for (int i = 0; i < SM; ++i) {
     const int rl = xrow0 + SUB * i + fr;
-    float sm = 1.f;
-    if (KIND == KIND_FP8 || KIND == KIND_INT8) sm = sxf[min(m0 + rl, M - 1)];
 #pragma unroll
     for (int j = 0; j < SN; ++j) {
 #pragma unroll
@@ -292,9 +317,9 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
         for (int r = 0; r < 4; ++r) {
           const acc_e a = acc[j][i][4 * q + r];
           if constexpr (KIND == KIND_FP8) {
-            v[r] = a * (sm * swf[min(n0 + cl + r, N - 1)]);
+            v[r] = a * (esm[i] * esn[j][q][r]);
           } else if constexpr (KIND == KIND_INT8) {
-            v[r] = __fmul_rn(__fmul_rn((float)a, sm), swf[min(n0 + cl + r, N - 1)]);
+            v[r] = __fmul_rn(__fmul_rn((float)a, esm[i]), esn[j][q][r]);
           } else {
             v[r] = a;
           }
