@@ -1,15 +1,23 @@
 """Benchmark: W8A8 FP8 linear layers at 8B-model prefill shapes on one MI355X.
 
-One step = the four prefill linears of an 8B model at M = 2048 tokens (QKV 4096->6144,
-O 4096->4096, gate+up 4096->28672, down 14336->4096), each as dynamic per-token E4M3FN
-quantization of its bf16 activations followed by the FP8 GEMM with the fused
-diag(s_x) . diag(s_w) epilogue writing bf16. Weights are quantized per output channel
-once, before timing (static weights). Inputs are seeded synthetic draws (module
-`synthetic`), resident in HBM before the timed region.
+Default workload ("prefill"): one step = the four prefill linears of an 8B model at
+M = 2048 tokens (QKV 4096->6144, O 4096->4096, gate+up 4096->28672, down 14336->4096), each
+as dynamic per-token E4M3FN quantization of its bf16 activations followed by the FP8 GEMM
+with the fused diag(s_x) . diag(s_w) epilogue writing bf16. Weights are quantized per
+output channel once, before timing (static weights). Inputs are seeded synthetic draws
+(module `synthetic`), resident in HBM before the timed region.
 
 Prints one JSON line: throughput in TFLOP/s (2MNK per GEMM, quantize time included), the
 GEMM kernel's roofline position (per-launch duration from HIP events on the launch
 stream), per-kernel figures, and the CPU oracle timed on a bounded sample.
+
+Other workloads (`--workload decode|blockscaled|mxfp4|all`) print one JSON line each:
+  decode       few-token sweep M in {1,8,32,128,512}, K = 4096, N in {4096, 14336}, FP8 and
+               SmoothQuant INT8 (smoothing folded offline); weights rotated over >512 MB
+               of copies so that no call finds them in the 256 MB last-level cache.
+  blockscaled  M = 4096, K = 7168, N = 18432 with 1x128 activation groups and 128x128
+               weight blocks (group quantize + block-scaled GEMM timed).
+  mxfp4        M = N = K = 8192, MXFP4 operands (MX quantize of X + FP4 GEMM timed).
 """
 
 from __future__ import annotations
@@ -17,6 +25,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -25,7 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (INT8: 5000 TOPS)
+FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_gemm_prefill_8b_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "fp4_w8a8_quantized_amd", "csrc", f)
@@ -37,9 +47,11 @@ def _parse_args():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="prefill",
+                   choices=["prefill", "decode", "blockscaled", "mxfp4", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=256,
-                   help="tokens per linear in the oracle sample (rows are independent)")
+                   help="tokens per linear in the prefill oracle sample (rows are independent)")
     return p.parse_args()
 
 
@@ -70,7 +82,47 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(layers, rows: int):
+def _threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((i.get("num_threads", 1) for i in threadpool_info()), default=1))
+    except Exception:  # pragma: no cover
+        return 1
+
+
+class Ctx:
+    """Device, stream and the raw C ABI handle shared by the workloads."""
+
+    def __init__(self):
+        import torch
+        import fp4_w8a8_quantized_amd as w8
+        self.torch, self.w8 = torch, w8
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.L = w8.lib()
+        self.stream = torch.cuda.current_stream(self.dev)
+        self.sh = self.stream.cuda_stream
+
+    def bf16(self, bits):
+        import numpy as np
+        return self.torch.from_numpy(bits.view(np.int16)).view(self.torch.bfloat16).to(self.dev)
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def check(self, st):
+        assert st == 0, self.w8.status_string(st)
+
+
+def _base_record(args, metric, value, unit, ms_per_step, dtype, config, higher=True):
+    return {"metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": higher, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+            "data": "synthetic", "config": config}
+
+
+# ----------------------------------------------------------------------------- prefill
+def prefill_cpu_baseline(layers, rows: int):
     """The oracle as it stands on a sample of the same step: `rows` tokens of each linear
     (per-token work is row-independent), weights quantized beforehand (untimed, like the
     GPU path). Returns the record for the JSON line."""
@@ -78,11 +130,6 @@ def cpu_baseline(layers, rows: int):
     from oracle import gemm as G
     from oracle import quant as Q
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = 1
     prepared = []
     for name, xb, wb in layers:
         wq, sw = Q.quantize_weight_per_channel_fp8(wb)
@@ -95,72 +142,45 @@ def cpu_baseline(layers, rows: int):
         flops += 2.0 * xs.shape[0] * wq.shape[0] * wq.shape[1]
         np.asarray(y).sum()
     dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": _threads(),
             "kind": "oracle",
             "sample": f"{rows} of 2048 tokens of each of the 4 prefill linears (quantize + fp64 "
                       f"contraction + scales), weights pre-quantized untimed; {dt:.1f} s"}
 
 
-def main():
-    args = _parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
-              "multi-GPU path: the method shards along tokens or output channels with no "
-              "exchange, so the per-GPU kernel is what is measured.", file=sys.stderr)
-        sys.exit(2)
-
+def run_prefill(args, c: Ctx):
     import numpy as np
-    import torch
-
-    import fp4_w8a8_quantized_amd as w8
     import synthetic
+    torch, w8, L, sh, stream = c.torch, c.w8, c.L, c.sh, c.stream
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    # ---- inputs (host generation, then resident in HBM)
     layers = [synthetic.prefill(i) for i in range(len(synthetic.PREFILL_SHAPES))]
     dl = []
     for name, xb, wb in layers:
-        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-        w = torch.from_numpy(wb.view(np.int16)).view(torch.bfloat16).to(dev)
+        x, w = c.bf16(xb), c.bf16(wb)
         wq, sw = w8.quantize_weight_per_channel(w)             # offline: static weights
         del w
         M, K = x.shape
         N = wq.shape[0]
-        xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=dev)
-        sx = torch.empty((M,), dtype=torch.float32, device=dev)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=c.dev)
+        sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
         dl.append(dict(name=name, x=x, xq=xq, sx=sx, wq=wq, sw=sw, y=y, M=M, N=N, K=K))
     torch.cuda.synchronize()
 
-    L = w8.lib()
-    stream = torch.cuda.current_stream(dev)
-    sh = stream.cuda_stream
-
     def launch_layer(d):
-        st = L.w8a8_quantize_per_token(d["x"].data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
-                                       d["sx"].data_ptr(), sh)
-        assert st == 0, w8.status_string(st)
-        st = L.w8a8_gemm(d["xq"].data_ptr(), d["sx"].data_ptr(), d["wq"].data_ptr(),
-                         d["sw"].data_ptr(), d["M"], d["N"], d["K"], 0, d["y"].data_ptr(), sh)
-        assert st == 0, w8.status_string(st)
-
-    def step():
-        for d in dl:
-            launch_layer(d)
+        c.check(L.w8a8_quantize_per_token(d["x"].data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
+                                          d["sx"].data_ptr(), sh))
+        c.check(L.w8a8_gemm(d["xq"].data_ptr(), d["sx"].data_ptr(), d["wq"].data_ptr(),
+                            d["sw"].data_ptr(), d["M"], d["N"], d["K"], 0, d["y"].data_ptr(), sh))
 
     for _ in range(args.warmup):
-        step()
+        for d in dl:
+            launch_layer(d)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, with HIP events around every launch on the launch stream
+    # timed region: K steps, with HIP events around every launch on the launch stream
     nl = len(dl)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-            torch.cuda.Event(enable_timing=True)) for _ in range(nl)] for _ in range(args.steps)]
+    ev = [[(c.event(), c.event(), c.event()) for _ in range(nl)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -207,37 +227,261 @@ def main():
                              "quant_GBps": round(q_bytes[i] / (q_ms[i] * 1e-3) / 1e9, 1)}
                  for i, d in enumerate(dl)}
 
-    rec = {
-        "metric": "W8A8 FP8 GEMM TFLOP/s (quant+GEMM+epilogue) at 8B shapes; % of FP8 MFMA peak",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3fn",
-        "data": "synthetic",
-        "config": {"workload": "8B-style prefill FP8 W8A8 linears, M=2048 tokens, "
-                               "(K,N) in {(4096,6144),(4096,4096),(4096,28672),(14336,4096)}, "
-                               "per-token/per-channel scales, bf16 out",
-                   "tokens": 2048, "shapes_KN": [[d["K"], d["N"]] for d in dl]},
-        "pct_of_fp8_peak": round(100.0 * value / FP8_PEAK_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": traffic},
-        "kernels": {"gemm_fp8_mean_us": round(float(g_ms.mean()) * 1e3, 2),
-                    "quantize_fp8_mean_us": round(float(q_ms.mean()) * 1e3, 2),
-                    "quantize_fp8_GBps": round(q_gbps, 1),
-                    "quantize_fp8_hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
-                    "per_layer": per_layer,
-                    "gemm_source_sha256_16": gemm_source_hash()},
-    }
+    rec = _base_record(
+        args, "W8A8 FP8 GEMM TFLOP/s (quant+GEMM+epilogue) at 8B shapes; % of FP8 MFMA peak",
+        value, "TFLOP/s", ms_per_step, "fp8_e4m3fn",
+        {"workload": "8B-style prefill FP8 W8A8 linears, M=2048 tokens, "
+                     "(K,N) in {(4096,6144),(4096,4096),(4096,28672),(14336,4096)}, "
+                     "per-token/per-channel scales, bf16 out",
+         "tokens": 2048, "shapes_KN": [[d["K"], d["N"]] for d in dl]})
+    rec["pct_of_fp8_peak"] = round(100.0 * value / FP8_PEAK_TFLOPS, 2)
+    rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                       "traffic": traffic}
+    rec["kernels"] = {"gemm_fp8_mean_us": round(float(g_ms.mean()) * 1e3, 2),
+                      "quantize_fp8_mean_us": round(float(q_ms.mean()) * 1e3, 2),
+                      "quantize_fp8_GBps": round(q_gbps, 1),
+                      "quantize_fp8_hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+                      "per_layer": per_layer,
+                      "gemm_source_sha256_16": gemm_source_hash()}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(layers, args.cpu_rows)
-    print(json.dumps(rec), flush=True)
+        rec["cpu_baseline"] = prefill_cpu_baseline(layers, args.cpu_rows)
+    return rec
+
+
+# ----------------------------------------------------------------------------- decode
+def decode_cpu_baseline():
+    """Oracle on the M = 8, N = 4096 decode case, FP8 path (quantize + fp64 contraction)."""
+    import numpy as np
+    import synthetic
+    from oracle import gemm as G
+    from oracle import quant as Q
+    x = synthetic.decode_x()[:8]
+    wq, sw = Q.quantize_weight_per_channel_fp8(synthetic.decode_w(4096))
+    reps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < 2.0:
+        xq, sx = Q.quantize_per_token_fp8(x)
+        np.asarray(G.gemm_fp8_ref(xq, sx, wq, sw)).sum()
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    byt = 4096 * 4096 + 8 * 4096 + 2 * 8 * 4096
+    return {"value": round(byt / dt / 1e9, 3), "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"M=8, N=4096, K=4096 FP8 (quantize + fp64 contraction + scales), "
+                      f"weights pre-quantized; {reps} repetitions, {dt * 1e3:.1f} ms each"}
+
+
+def run_decode(args, c: Ctx):
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh, stream = c.torch, c.w8, c.L, c.sh, c.stream
+    K = synthetic.DECODE_K
+    xall = c.bf16(synthetic.decode_x())
+    xcal = c.bf16(synthetic.decode_calibration())
+    cases = []
+    for N in synthetic.DECODE_NS:
+        w = c.bf16(synthetic.decode_w(N))
+        wq8, sw8 = w8.quantize_weight_per_channel(w)
+        s = w8.smoothquant_scales(w8.channel_absmax(xcal), w8.channel_absmax(w), 0.5)
+        wqi, swi = w8.quantize_weight_per_channel(w8.smooth_apply(w, s, "weight"), "int8")
+        xh = w8.smooth_apply(xall, s, "activation")   # folded into the previous layer offline
+        del w
+        copies = max(2, math.ceil(600e6 / (N * K)))
+        weights = {0: ([wq8] + [wq8.clone() for _ in range(copies - 1)], sw8, xall),
+                   1: ([wqi] + [wqi.clone() for _ in range(copies - 1)], swi, xh)}
+        torch.cuda.synchronize()
+        for M in synthetic.DECODE_MS:
+            for fmt in (0, 1):
+                ws, sw, xsrc = weights[fmt]
+                x = xsrc[:M]
+                xq = torch.empty((M, K), dtype=torch.float8_e4m3fn if fmt == 0 else torch.int8, device=c.dev)
+                sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+
+                def launch(i, e=None):
+                    if e:
+                        e[0].record(stream)
+                    c.check(L.w8a8_quantize_per_token(x.data_ptr(), M, K, fmt, xq.data_ptr(), sx.data_ptr(), sh))
+                    if e:
+                        e[1].record(stream)
+                    c.check(L.w8a8_gemm(xq.data_ptr(), sx.data_ptr(), ws[i % copies].data_ptr(),
+                                        sw.data_ptr(), M, N, K, fmt, y.data_ptr(), sh))
+                    if e:
+                        e[2].record(stream)
+
+                for i in range(max(args.warmup, 3)):
+                    launch(i)
+                R = 3 * copies
+                ev = [(c.event(), c.event(), c.event()) for _ in range(R)]
+                torch.cuda.synchronize()
+                for i in range(R):
+                    launch(i, ev[i])
+                torch.cuda.synchronize()
+                q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+                g_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+                byt = N * K + M * K + 2 * M * N + 4 * (M + N)
+                flops = 2.0 * M * N * K
+                attain = min(FP8_PEAK_TFLOPS, flops / byt * HBM_PEAK_GBPS / 1e3)   # TFLOP/s
+                cases.append({"M": M, "N": N, "fmt": "fp8" if fmt == 0 else "int8",
+                              "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2),
+                              "gemm_GBps": round(byt / g_us / 1e3, 1),
+                              "gemm_tflops": round(flops / g_us / 1e6, 2),
+                              "roofline_frac": round(flops / g_us / 1e6 / attain, 4)})
+        del weights
+        torch.cuda.empty_cache()
+    hbm = [cs for cs in cases if cs["fmt"] == "fp8" and cs["M"] <= 128]
+    tot_bytes = sum(cs["N"] * K + cs["M"] * K + 2 * cs["M"] * cs["N"] for cs in hbm)
+    tot_us = sum(cs["gemm_us"] for cs in hbm)
+    achieved = tot_bytes / tot_us / 1e3
+    total_us = sum(cs["gemm_us"] + cs["quant_us"] for cs in cases)
+    rec = _base_record(
+        args, "W8A8 decode GEMM HBM GB/s (FP8, M<=128, K=4096, N in {4096,14336})", achieved,
+        "GB/s", total_us / 1e3, "fp8_e4m3fn+int8",
+        {"workload": "decode sweep M in {1,8,32,128,512}, K=4096, N in {4096,14336}; FP8 per-token "
+                     "and SmoothQuant INT8 (alpha 0.5, smoothing folded offline); weights rotated "
+                     "over >512 MB of copies", "K": K})
+    rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    rec["cases"] = cases
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = decode_cpu_baseline()
+    return rec
+
+
+# ----------------------------------------------------------------------------- block-scaled
+def _timed_pair(args, c: Ctx, first, second):
+    """Warm up, then time `steps` of first() + second() with events around each."""
+    import numpy as np
+    for _ in range(args.warmup):
+        first()
+        second()
+    ev = [(c.event(), c.event(), c.event()) for _ in range(args.steps)]
+    c.torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(c.stream)
+        first()
+        e[1].record(c.stream)
+        second()
+        e[2].record(c.stream)
+    c.torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    a = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    return wall, a, b
+
+
+def run_blockscaled(args, c: Ctx):
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh = c.torch, c.w8, c.L, c.sh
+    M, K, N = synthetic.BLOCKSCALED_SHAPE
+    xb, wb = synthetic.blockscaled()
+    x = c.bf16(xb)
+    w = c.bf16(wb)
+    wq, sw = w8.quantize_weight_block(w)
+    del w
+    xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=c.dev)
+    sx = torch.empty((M, K // 128), dtype=torch.float32, device=c.dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+    torch.cuda.synchronize()
+    wall, q_s, g_s = _timed_pair(
+        args, c,
+        lambda: c.check(L.w8a8_quantize_per_token_group(x.data_ptr(), M, K, xq.data_ptr(), sx.data_ptr(), sh)),
+        lambda: c.check(L.w8a8_gemm_blockscaled(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(),
+                                                M, N, K, y.data_ptr(), sh)))
+    flops = 2.0 * M * N * K
+    achieved = flops / g_s / 1e12
+    rec = _base_record(args, "Block-scaled FP8 GEMM TFLOP/s (group quant + GEMM), % of FP8 MFMA peak",
+                       flops / wall / 1e12, "TFLOP/s", wall * 1e3, "fp8_e4m3fn",
+                       {"workload": "1x128 activation groups, 128x128 weight blocks, fp32 promotion "
+                                    "per 128-K group", "M": M, "K": K, "N": N})
+    rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    q_bytes = 3.0 * M * K + 4.0 * M * (K // 128)
+    rec["kernels"] = {"gemm_us": round(g_s * 1e6, 1), "group_quant_us": round(q_s * 1e6, 1),
+                      "group_quant_GBps": round(q_bytes / q_s / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        from oracle import gemm as G
+        from oracle import quant as Q
+        rows, cols = 64, 2048
+        owq, osw = Q.quantize_weight_block_fp8(wb[:cols])
+        t0 = time.perf_counter()
+        oxq, osx = Q.quantize_per_token_group_fp8(xb[:rows])
+        np.asarray(G.gemm_blockscaled_ref(oxq, osx, owq, osw)).sum()
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(2.0 * rows * cols * K / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": _threads(), "kind": "oracle",
+                               "sample": f"{rows} tokens x {cols} outputs x K={K} (group quantize + "
+                                         f"per-group fp64 contraction), weights pre-quantized; {dt:.1f} s"}
+    return rec
+
+
+# ----------------------------------------------------------------------------- MXFP4
+def run_mxfp4(args, c: Ctx):
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh = c.torch, c.w8, c.L, c.sh
+    M, K, N = synthetic.MXFP4_SHAPE
+    xb, wb = synthetic.mxfp4()
+    x = c.bf16(xb)
+    w = c.bf16(wb)
+    wq, sw = w8.quantize_mxfp4(w)
+    del w
+    xq = torch.empty((M, K // 2), dtype=torch.uint8, device=c.dev)
+    sx = torch.empty((M, K // 32), dtype=torch.uint8, device=c.dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+    torch.cuda.synchronize()
+    wall, q_s, g_s = _timed_pair(
+        args, c,
+        lambda: c.check(L.w8a8_quantize_mxfp4(x.data_ptr(), M, K, xq.data_ptr(), sx.data_ptr(), sh)),
+        lambda: c.check(L.w8a8_gemm_mxfp4(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(),
+                                          M, N, K, y.data_ptr(), sh)))
+    flops = 2.0 * M * N * K
+    achieved = flops / g_s / 1e12
+    rec = _base_record(args, "MXFP4 GEMM TFLOP/s (MX quantize + FP4 GEMM), % of FP4 MFMA peak",
+                       flops / wall / 1e12, "TFLOP/s", wall * 1e3, "fp4_e2m1+e8m0",
+                       {"workload": "OCP MXFP4 operands (E2M1, E8M0 per 32 along K)", "M": M, "K": K, "N": N})
+    rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None}
+    q_bytes = 2.5 * M * K + M * K / 32
+    rec["kernels"] = {"gemm_us": round(g_s * 1e6, 1), "mx_quant_us": round(q_s * 1e6, 1),
+                      "mx_quant_GBps": round(q_bytes / q_s / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        from oracle import gemm as G
+        from oracle import quant as Q
+        rows, cols = 64, 2048
+        owq, osw = Q.quantize_mxfp4(wb[:cols])
+        t0 = time.perf_counter()
+        oxq, osx = Q.quantize_mxfp4(xb[:rows])
+        np.asarray(G.gemm_mxfp4_ref(oxq, osx, owq, osw)).sum()
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(2.0 * rows * cols * K / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": _threads(), "kind": "oracle",
+                               "sample": f"{rows} tokens x {cols} outputs x K={K} (MX quantize + fp64 "
+                                         f"contraction of decoded blocks), weights pre-quantized; {dt:.1f} s"}
+    return rec
+
+
+def main():
+    args = _parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path: the method shards along tokens or output channels with no "
+              "exchange, so the per-GPU kernel is what is measured.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    c = Ctx()
+    runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
+            "mxfp4": run_mxfp4}
+    names = list(runs) if args.workload == "all" else [args.workload]
+    for name in names:
+        rec = runs[name](args, c)
+        print(json.dumps(rec), flush=True)
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -384,6 +384,7 @@ static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, cons
 // also retires their scale loads.
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st) {
+  if (use_skinny(M, N)) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st);
   if (fmt == 1) {
     static const int c[3] = {256, 192, 128};
     switch (pick_bn(M, N, c, 3)) {

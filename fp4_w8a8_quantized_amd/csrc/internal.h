@@ -18,6 +18,13 @@ hipError_t launch_quantize_mxfp4(const void* x, int64_t R, int64_t K, void* q, u
 
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st);
+// Few-token form of launch_gemm: weights streamed by 16-, 32- or 64-row workgroups that
+// split K among their waves. It wins while the weights dominate the traffic: up to 64
+// tokens, and up to 128 on layers of at most 8192 outputs (measured crossover against the
+// tiled kernel at K = 4096).
+inline bool use_skinny(int64_t M, int64_t N) { return M <= 64 || (M <= 128 && N <= 8192); }
+hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
+                              int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st);
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                    hipStream_t st);

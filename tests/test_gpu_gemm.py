@@ -66,6 +66,22 @@ def test_fp8_ragged(M, N, K):
     _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
 
 
+# Few-token path (M <= 64, or M <= 128 with N <= 8192): every 16-row bucket edge, N not a multiple of 4 or 16, one K
+# step (most waves idle), K step counts that need a second weight chunk per wave, wide
+# layers (N > 8192: 32 or 64 weight rows per workgroup, with a ragged last workgroup), and
+# the first sizes on the tiled kernel (M = 129; M = 65..128 with N > 8192).
+SKINNY_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (65, 100, 2048),
+                (128, 130, 1152), (129, 257, 256), (2, 18, 14336), (16, 9000, 256),
+                (32, 8200, 384), (64, 10000, 1152), (128, 8193, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_CASES)
+def test_fp8_few_tokens(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, 11 * M + 5 * N + K)
+    _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("i", [0, 1, 2, 3])
 def test_fp8_prefill_full_size_sampled(i):
     """The 8B prefill linears at full size, in the bench's launch configuration; codes of
@@ -147,6 +163,14 @@ def test_int8_ragged(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
     xcal, _ = _xw(64, 1, K, K)
+    _int8_chain(xb, xcal, wb, 0.5, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_CASES)
+def test_int8_few_tokens(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, 13 * M + 3 * N + K)
+    xcal, _ = _xw(64, 1, K, K + 1)
     _int8_chain(xb, xcal, wb, 0.5, f"{M}x{N}x{K}")
 
 
