@@ -52,6 +52,13 @@ def _parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=256,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB three times (the reference for "
+                        "rocprofv3's FETCH_SIZE / WRITE_SIZE) and exit")
+    p.add_argument("--traffic-summary", nargs=4, metavar=("COPY_FETCH", "COPY_WRITE", "GEMM_FETCH", "GEMM_WRITE"),
+                   help="write the traffic summary from four rocprofv3 counter_collection.csv files "
+                        "(copy and prefill runs, FETCH_SIZE then WRITE_SIZE) and exit; no GPU needed")
+    p.add_argument("--copy-mib", type=int, default=256, help="size used with --calibrate-copy")
     return p.parse_args()
 
 
@@ -80,6 +87,64 @@ def measured_traffic():
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _counter_rows(path):
+    """(kernel name, counter value) per dispatch from a rocprofv3 counter_collection.csv."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            val = r.get("Counter_Value") or r.get("Counter-Value")
+            if val is not None:
+                rows.append((name, float(val)))
+    return rows
+
+
+def traffic_summary(args):
+    """HBM bytes per FP8 GEMM launch of the prefill step from FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reports for a plain copy of
+    args.copy_mib MiB (which moves exactly that many bytes each way)."""
+    import numpy as np
+    cf, cw, gf, gw = args.traffic_summary
+    copy_bytes = args.copy_mib * 2**20
+
+    def copy_kib(path):
+        v = [x for n, x in _counter_rows(path) if "opy" in n]
+        return float(np.median(v)) if v else float("nan")
+
+    def gemm_kib(path):
+        v = [x for n, x in _counter_rows(path) if "gemm_kernel" in n]
+        return float(np.mean(v)), len(v)
+
+    f_scale = copy_bytes / (copy_kib(cf) * 1024.0)
+    w_scale = copy_bytes / (copy_kib(cw) * 1024.0)
+    fk, nf = gemm_kib(gf)
+    wk, nw = gemm_kib(gw)
+    fetch = fk * 1024.0 * f_scale
+    write = wk * 1024.0 * w_scale
+    import synthetic
+    alg = np.mean([2048 * K + N * K + 2 * 2048 * N for _, K, N in synthetic.PREFILL_SHAPES])
+    text = f"""# HBM traffic of the FP8 GEMM in the 8B prefill step (mean per launch over QKV, O, gate+up, down)
+# commands (from the repository root, on one MI355X; each --pmc pass in a run of its own):
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o copy -- python3 bench.py --calibrate-copy {args.copy_mib}
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o copy -- python3 bench.py --calibrate-copy {args.copy_mib}
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_gemm_fetch -o gemm -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_gemm_write -o gemm -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+#   python3 bench.py --traffic-summary <the four counter_collection.csv files> (this file)
+# copy calibration ({args.copy_mib} MiB each way): FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}
+# GEMM dispatches: {nf} (FETCH_SIZE pass), {nw} (WRITE_SIZE pass)
+# algorithmic bytes per launch (MK + NK + 2MN, mean over the four shapes): {alg:.0f}
+gemm_source_sha256_16 = {gemm_source_hash()}
+fetch_bytes_per_launch = {fetch:.0f}
+write_bytes_per_launch = {write:.0f}
+hbm_bytes_per_launch = {fetch + write:.0f}
+traffic_over_algorithmic = {(fetch + write) / alg:.3f}
+"""
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write(text)
+    print(text)
 
 
 def _threads() -> int:
@@ -470,10 +535,22 @@ def main():
               "exchange, so the per-GPU kernel is what is measured.", file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_summary:
+        traffic_summary(args)
+        return
     import torch
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2**20
+        src = torch.ones((n,), dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n}), flush=True)
+        return
     c = Ctx()
     runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
             "mxfp4": run_mxfp4}

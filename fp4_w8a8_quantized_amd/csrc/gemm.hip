@@ -227,6 +227,18 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     const int kdma = min(ks + STAGES, ksteps - 1);
     const uint8_t* X = lds + ((ks + 1) % STAGES) * STAGE;
     const uint8_t* W = X + XT;
+    // Block-scaled: each MFMA is one 128-wide K group; its fp32 product is promoted into
+    // the running sum (times s_x[m,g] s_w[n/128,g], one factor per lane) PD MFMAs later,
+    // so that the promotion never waits on the MFMA it follows and PD products are in
+    // flight in distinct registers.
+    constexpr int PD = 4;
+    f32x4 pp[PD];
+    auto promote = [&](int t) {
+      if constexpr (KIND == KIND_BLOCK) {
+        const int ti = t / SN, tj = t % SN;
+        acc[tj][ti] += pp[t % PD] * (bsx[ti] * bsw[tj]);
+      }
+    };
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
 #pragma unroll
@@ -234,8 +246,10 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
         if constexpr (KIND == KIND_FP8) {
           acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
         } else if constexpr (KIND == KIND_BLOCK) {
-          const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-          acc[j][i] += p * (bsx[i] * bsw[j]);
+          const int t = i * SN + j;
+          if (t >= PD) promote(t - PD);
+          pp[t % PD] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);      // keep the promotion PD MFMAs behind
         } else if constexpr (KIND == KIND_INT8) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -263,6 +277,10 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     }
 #pragma unroll
     for (int j = SM; j < SN; ++j) wnxt[j] = frag(W + (wrow0 + SUB * j) * 128);
+    if constexpr (KIND == KIND_BLOCK) {
+#pragma unroll
+      for (int t = SM * SN - PD; t < SM * SN; ++t) promote(t);
+    }
 #pragma unroll
     for (int i = 0; i < SM; ++i) { bsx[i] = nsx[i]; esx[i] = nex[i]; }
 #pragma unroll
