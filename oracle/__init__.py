@@ -24,8 +24,10 @@ Pinning status (what each part is checked against lives in ``tests/test_oracle_*
 * gemm.py         pinned (brute force, scale-factoring identity, [P-FP8FP4] worked example)
 * smoothquant.py  pinned (closed forms printed on [P-LOWBIT] Try-it 02 and [P-FP8FP4])
 * roofline.py     pinned (numbers printed on [P-FP8FP4] and [P-LOWBIT] §5)
+* epilogue.py     pinned (options off = the plain references; SiLU closed forms and an
+                  independent routine; hand-computed INT8 order and FP8-code examples)
 """
 
-from . import formats, quant, gemm, smoothquant, roofline  # noqa: F401
+from . import formats, quant, gemm, smoothquant, roofline, epilogue  # noqa: F401
 
-__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline"]
+__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue"]
