@@ -18,6 +18,9 @@ Other workloads (`--workload decode|blockscaled|mxfp4|all`) print one JSON line 
   blockscaled  M = 4096, K = 7168, N = 18432 with 1x128 activation groups and 128x128
                weight blocks (group quantize + block-scaled GEMM timed).
   mxfp4        M = N = K = 8192, MXFP4 operands (MX quantize of X + FP4 GEMM timed).
+  epilogue     the prefill linears with the full epilogue: + bf16 bias, SiLU, and FP8
+               output requantized with a static scale (calibrated once, untimed), against
+               the plain bf16 epilogue on the same inputs.
 """
 
 from __future__ import annotations
@@ -48,7 +51,7 @@ def _parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "blockscaled", "mxfp4", "all"])
+                   choices=["prefill", "decode", "blockscaled", "mxfp4", "epilogue", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=256,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
@@ -314,6 +317,68 @@ def run_prefill(args, c: Ctx):
     return rec
 
 
+# ----------------------------------------------------------------------------- epilogue
+def run_epilogue(args, c: Ctx):
+    """Prefill linears: quantize + GEMM with bias, SiLU and FP8 output vs the plain GEMM."""
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh = c.torch, c.w8, c.L, c.sh
+    dl = []
+    for i in range(len(synthetic.PREFILL_SHAPES)):
+        name, xb, wb = synthetic.prefill(i)
+        x, w = c.bf16(xb), c.bf16(wb)
+        wq, sw = w8.quantize_weight_per_channel(w)
+        del w
+        M, K = x.shape
+        N = wq.shape[0]
+        xq, sx = w8.quantize_per_token(x)
+        rng = np.random.default_rng(1000 + i)
+        bias = c.bf16(synthetic.to_bf16_bits(rng.standard_normal(N) * 0.1))
+        y0 = w8.gemm(xq, sx, wq, sw)                          # calibration of the static scale
+        s_out = float(torch.nn.functional.silu(y0.float() + bias.float()).abs().max()) / 448.0
+        y8 = torch.empty((M, N), dtype=torch.float8_e4m3fn, device=c.dev)
+        dl.append(dict(name=name, x=x, xq=xq, sx=sx, wq=wq, sw=sw, y0=y0, y8=y8, bias=bias,
+                       s_out=s_out, M=M, N=N, K=K))
+    torch.cuda.synchronize()
+
+    def quant(d):
+        c.check(L.w8a8_quantize_per_token(d["x"].data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
+                                          d["sx"].data_ptr(), sh))
+
+    def plain(d):
+        c.check(L.w8a8_gemm(d["xq"].data_ptr(), d["sx"].data_ptr(), d["wq"].data_ptr(), d["sw"].data_ptr(),
+                            d["M"], d["N"], d["K"], 0, d["y0"].data_ptr(), sh))
+
+    def full(d):
+        c.check(L.w8a8_gemm_ex(d["xq"].data_ptr(), d["sx"].data_ptr(), d["wq"].data_ptr(), d["sw"].data_ptr(),
+                               d["M"], d["N"], d["K"], 0, d["bias"].data_ptr(), 2, 1, d["s_out"],
+                               d["y8"].data_ptr(), sh))
+
+    res = {}
+    for tag, fn in (("plain_bf16", plain), ("bias_silu_fp8", full)):
+        per = {}
+        tot_g, tot_w = 0.0, 0.0
+        for d in dl:
+            wall, q_s, g_s = _timed_pair(args, c, lambda d=d: quant(d), lambda d=d, fn=fn: fn(d))
+            per[d["name"]] = round(2.0 * d["M"] * d["N"] * d["K"] / g_s / 1e12, 1)
+            tot_g += g_s
+            tot_w += wall
+        res[tag] = {"gemm_tflops_per_layer": per, "gemm_us_total": round(tot_g * 1e6, 1),
+                    "step_ms": round(tot_w * 1e3, 4)}
+    flops = sum(2.0 * d["M"] * d["N"] * d["K"] for d in dl)
+    g_full = res["bias_silu_fp8"]["gemm_us_total"] * 1e-6
+    achieved = flops / len(dl) / (g_full / len(dl)) / 1e12
+    rec = _base_record(args, "W8A8 FP8 GEMM TFLOP/s with bias + SiLU + FP8 requantized output, 8B prefill",
+                       flops / (res["bias_silu_fp8"]["step_ms"] * 1e-3) / 1e12, "TFLOP/s",
+                       res["bias_silu_fp8"]["step_ms"], "fp8_e4m3fn",
+                       {"workload": "8B-style prefill FP8 W8A8 linears at M=2048 with the full epilogue "
+                                    "(bf16 bias, SiLU, E4M3FN output with a static scale)", "tokens": 2048})
+    rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    rec["variants"] = res
+    return rec
+
+
 # ----------------------------------------------------------------------------- decode
 def decode_cpu_baseline():
     """Oracle on the M = 8, N = 4096 decode case, FP8 path (quantize + fp64 contraction)."""
@@ -553,6 +618,7 @@ def main():
         return
     c = Ctx()
     runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
+            "epilogue": run_epilogue,
             "mxfp4": run_mxfp4}
     names = list(runs) if args.workload == "all" else [args.workload]
     for name in names:

@@ -20,11 +20,11 @@ import torch
 
 __all__ = [
     "lib", "library_path", "status_string", "W8A8Error",
-    "quantize_per_token", "quantize_weight_per_channel", "gemm", "linear",
+    "quantize_per_token", "quantize_weight_per_channel", "gemm", "gemm_ex", "linear",
     "quantize_per_token_group", "quantize_weight_block", "gemm_blockscaled",
     "quantize_mxfp4", "gemm_mxfp4",
     "channel_absmax", "smoothquant_scales", "smooth_apply",
-    "FMT_E4M3FN", "FMT_INT8",
+    "FMT_E4M3FN", "FMT_INT8", "ACTIVATIONS",
 ]
 
 FMT_E4M3FN = 0
@@ -43,6 +43,8 @@ _SIGNATURES = {
     "w8a8_quantize_per_token": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp],
     "w8a8_quantize_weight_per_channel": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp],
+    "w8a8_gemm_ex": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
+                     _c_int, _c_float, _c_vp, _c_vp],
     "w8a8_quantize_per_token_group": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "w8a8_quantize_weight_block": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
@@ -156,6 +158,47 @@ def gemm(xq: torch.Tensor, sx: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor,
         raise ValueError("out must be [M, N]")
     _check(lib().w8a8_gemm(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(), M, N, K, f,
                            y.data_ptr(), _stream(xq)), "w8a8_gemm")
+    return y
+
+
+ACTIVATIONS = {"none": 0, "relu": 1, "silu": 2}
+
+
+def gemm_ex(xq: torch.Tensor, sx: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor,
+            bias: torch.Tensor | None = None, act: str = "none", out_scale: float | None = None,
+            out: torch.Tensor | None = None) -> torch.Tensor:
+    """The scaled GEMM with the full epilogue: + bias (bf16 [N]), activation ("none",
+    "relu", "silu"), then bf16 [M, N], or, when out_scale is given, E4M3FN codes of
+    clamp(v / out_scale, +-448) as float8_e4m3fn [M, N]."""
+    _dev(xq, "xq", (torch.float8_e4m3fn, torch.int8), 2)
+    f = FMT_INT8 if xq.dtype == torch.int8 else FMT_E4M3FN
+    _dev(wq, "wq", xq.dtype, 2)
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq disagree on K")
+    _dev(sx, "sx", torch.float32, 1)
+    _dev(sw, "sw", torch.float32, 1)
+    if sx.shape[0] != M or sw.shape[0] != N:
+        raise ValueError("scale lengths must be M and N")
+    if act not in ACTIVATIONS:
+        raise ValueError(f"unknown activation {act!r}")
+    bptr = None
+    if bias is not None:
+        _dev(bias, "bias", torch.bfloat16, 1)
+        if bias.shape[0] != N:
+            raise ValueError("bias length must be N")
+        bptr = bias.data_ptr()
+    fp8_out = out_scale is not None
+    ydt = torch.float8_e4m3fn if fp8_out else torch.bfloat16
+    y = out if out is not None else torch.empty((M, N), dtype=ydt, device=xq.device)
+    _dev(y, "out", ydt, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("out must be [M, N]")
+    _check(lib().w8a8_gemm_ex(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(), M, N, K, f,
+                              bptr, ACTIVATIONS[act], 1 if fp8_out else 0,
+                              float(out_scale) if fp8_out else 1.0, y.data_ptr(), _stream(xq)),
+           "w8a8_gemm_ex")
     return y
 
 

@@ -88,6 +88,23 @@ w8a8_status w8a8_gemm(const void* xq, const float* sx, const void* wq, const flo
   return hip_status(w8a8::launch_gemm(xq, sx, wq, sw, M, N, K, fmt, y_bf16, as_stream(stream)));
 }
 
+w8a8_status w8a8_gemm_ex(const void* xq, const float* sx, const void* wq, const float* sw,
+                         int64_t M, int64_t N, int64_t K, int fmt, const void* bias_bf16,
+                         int act, int out_fmt, float out_scale, void* y, void* stream) {
+  if (fmt != W8A8_FMT_E4M3FN && fmt != W8A8_FMT_INT8) return W8A8_ERR_UNSUPPORTED;
+  if (act != W8A8_ACT_NONE && act != W8A8_ACT_RELU && act != W8A8_ACT_SILU)
+    return W8A8_ERR_UNSUPPORTED;
+  if (out_fmt != W8A8_OUT_BF16 && out_fmt != W8A8_OUT_E4M3FN) return W8A8_ERR_UNSUPPORTED;
+  if (out_fmt == W8A8_OUT_E4M3FN && !(out_scale > 0.f && out_scale <= 3.4028234663852886e38f))
+    return W8A8_ERR_ARG;                                 // also rejects NaN and +inf
+  w8a8_status st = check_gemm(xq, sx, wq, sw, M, N, K, 128, K, y);
+  if (st != W8A8_OK || M == 0 || N == 0) return st;
+  if (bias_bf16 && !aligned16(bias_bf16)) return W8A8_ERR_ALIGN;
+  const w8a8::Epilogue ep{reinterpret_cast<const uint16_t*>(bias_bf16), act,
+                          out_fmt == W8A8_OUT_E4M3FN ? 1 : 0, out_scale, 1.f / out_scale};
+  return hip_status(w8a8::launch_gemm(xq, sx, wq, sw, M, N, K, fmt, y, as_stream(stream), ep));
+}
+
 w8a8_status w8a8_quantize_per_token_group(const void* x_bf16, int64_t M, int64_t K, void* xq,
                                           float* sx, void* stream) {
   w8a8_status st = check_dims(M, K);

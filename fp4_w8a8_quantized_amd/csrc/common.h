@@ -72,6 +72,40 @@ __device__ __forceinline__ float chunk_absmax(u32x4 v) {
   return m;
 }
 
+// An fp32 product and an fp32 sum, each rounded on its own. HIP compiles with contraction
+// on, and its __fmul_rn / __fadd_rn are the plain operators, so a product followed by a
+// sum could become one FMA (one rounding); these keep the two roundings the INT8
+// epilogue's fixed order asks for.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+__device__ __forceinline__ float add_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a + b;
+}
+
+// GEMM epilogue activation: 0 identity, 1 ReLU max(v, 0), 2 SiLU v / (1 + e^-v) (with the
+// hardware exponential and reciprocal; SiLU is compared within a tolerance).
+__device__ __forceinline__ float epi_activate(float v, int act) {
+  if (act == 1) return fmaxf(v, 0.f);
+  if (act == 2) return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+  return v;
+}
+
+// clamp(q, +-448); a NaN stays NaN (both comparisons are false).
+__device__ __forceinline__ float clamp448(float q) {
+  return q > 448.f ? 448.f : (q < -448.f ? -448.f : q);
+}
+
+// Requantization for an FP8 output, clamp(v / s, +-448). EXACT: the IEEE fp32 division
+// (the INT8 operand path, whose outputs are bit-exact); otherwise the product with the
+// fp32 reciprocal inv = 1/s (FP8 operands, whose outputs are compared within a tolerance).
+template <bool EXACT>
+__device__ __forceinline__ float epi_requant(float v, float s, float inv) {
+  return clamp448(EXACT ? v / s : v * inv);
+}
+
 // max(amax, 1e-8) / qmax with a NaN amax passed through (all-NaN row).
 __device__ __forceinline__ float amax_scale(float amax, float qmax) {
   float a = (amax != amax) ? amax : fmaxf(amax, 1e-8f);

@@ -72,11 +72,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 template <class T>
 __device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
 
-template <int BN, int KIND, int STAGES>
+template <int BN, int KIND, int STAGES, bool OF8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
             const uint8_t* __restrict__ wq, const void* __restrict__ swp, int M, int N,
-            int Kb, int ksteps, uint16_t* __restrict__ y, int tiles_m, int vec_store) {
+            int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
   constexpr bool MF32 = (KIND == KIND_INT8 || KIND == KIND_MXFP4);
   constexpr int SUB = MF32 ? 32 : 16;         // MFMA output tile edge
   constexpr int SM = 128 / SUB;               // X subtiles per wave (128 rows)
@@ -293,32 +293,37 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   }
   if (ks < ksteps) step(ks, wf0, wf1);
 
-  // ---- epilogue: scale + convert in registers, stage the bf16 tile through LDS (free
-  // once every in-flight load has landed and every wave left the loop), then write whole
-  // rows with 16-byte stores. Row stride is padded by 16 B (conflict-free 8-byte writes
-  // down a column); at BN = 256 the padding does not fit, so chunks are XOR-swizzled.
-  constexpr int RS = BN == 256 ? 512 : BN * 2 + 16;
+  // ---- epilogue: dequantize, add the bias, activate and convert in registers (bf16, or
+  // E4M3FN codes of clamp(v / s_out) when OF8), stage the tile through LDS (free once every
+  // in-flight load has landed and every wave left the loop), then write whole rows with
+  // 16-byte stores. Row stride is padded by 16 B (conflict-free writes down a column); a
+  // bf16 tile at BN = 256 does not fit with padding, so its chunks are XOR-swizzled.
+  constexpr int ES = OF8 ? 1 : 2;              // output bytes per element
+  constexpr bool SWZ = (BN == 256 && !OF8);
+  constexpr int RS = SWZ ? 512 : BN * ES + 16;
   static_assert(kBM * RS <= STAGES * STAGE, "output tile must fit in the pipeline LDS");
   auto opos = [&](int row, int byte) -> int {
-    return BN == 256 ? row * RS + ((((byte >> 4) ^ (row & 15)) << 4) | (byte & 15)) : row * RS + byte;
+    return SWZ ? row * RS + ((((byte >> 4) ^ (row & 15)) << 4) | (byte & 15)) : row * RS + byte;
   };
-  // The per-row and per-column scales this lane needs are loaded in one batch, so their
-  // latencies overlap, before the first epilogue barrier.
+  // The per-row and per-column scales (and biases) this lane needs are loaded in one
+  // batch, so their latencies overlap, before the first epilogue barrier.
   constexpr int NG = MF32 ? 4 : 1;            // runs of 4 columns per lane per subtile
   constexpr bool SCALED = (KIND == KIND_FP8 || KIND == KIND_INT8);
-  float esm[SM], esn[SN][NG][4];
+  float esm[SM], esn[SN][NG][4], ebias[SN][NG][4];
+  const bool has_bias = ep.bias != nullptr;
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = min(n0 + wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g) + r, N - 1);
+        if constexpr (SCALED) esn[j][q][r] = reinterpret_cast<const float*>(swp)[n];
+        ebias[j][q][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
+      }
   if constexpr (SCALED) {
-    const float* sxf = reinterpret_cast<const float*>(sxp);
-    const float* swf = reinterpret_cast<const float*>(swp);
 #pragma unroll
-    for (int i = 0; i < SM; ++i) esm[i] = sxf[min(m0 + xrow0 + SUB * i + fr, M - 1)];
-#pragma unroll
-    for (int j = 0; j < SN; ++j)
-#pragma unroll
-      for (int q = 0; q < NG; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          esn[j][q][r] = swf[min(n0 + wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g) + r, N - 1)];
+    for (int i = 0; i < SM; ++i) esm[i] = reinterpret_cast<const float*>(sxp)[min(m0 + xrow0 + SUB * i + fr, M - 1)];
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   lds_barrier();
@@ -337,32 +342,45 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
           if constexpr (KIND == KIND_FP8) {
             v[r] = a * (esm[i] * esn[j][q][r]);
           } else if constexpr (KIND == KIND_INT8) {
-            v[r] = __fmul_rn(__fmul_rn((float)a, esm[i]), esn[j][q][r]);
+            v[r] = mul_rn(mul_rn((float)a, esm[i]), esn[j][q][r]);
           } else {
             v[r] = a;
           }
+          if (has_bias) v[r] = add_rn(v[r], ebias[j][q][r]);
+          v[r] = epi_activate(v[r], ep.act);
         }
-        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+        if constexpr (OF8) {
+          constexpr bool EX = (KIND == KIND_INT8);
+          *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
+              pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
+                          epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
+        } else {
+          const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+        }
       }
     }
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   lds_barrier();
-  constexpr int CPR = BN / 8;                 // 16-byte chunks per output row
+  constexpr int EPC = 16 / ES;                 // output elements per 16-byte chunk
+  constexpr int CPR = BN / EPC;                // 16-byte chunks per output row
   for (int c = t; c < kBM * CPR; c += kThreads) {
     const int rl = c / CPR, ch = c - rl * CPR;
-    const int m = m0 + rl, n = n0 + ch * 8;
+    const int m = m0 + rl, n = n0 + ch * EPC;
     if (m >= M || n >= N) continue;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + opos(rl, ch * 16));
-    uint16_t* yr = y + (size_t)m * N;
-    if (vec_store && n + 7 < N) {
-      *reinterpret_cast<u32x4*>(yr + n) = v;
+    uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + ((size_t)m * N + n) * ES;
+    if (vec_store && n + EPC - 1 < N) {
+      *reinterpret_cast<u32x4*>(yr) = v;
     } else {
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (n + e < N) yr[n + e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      for (int e = 0; e < EPC; ++e) {
+        if (n + e >= N) break;
+        if constexpr (OF8) yr[e] = (uint8_t)((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        else reinterpret_cast<uint16_t*>(yr)[e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      }
     }
   }
 }
@@ -382,16 +400,18 @@ static int pick_bn(int64_t M, int64_t N, const int* cands, int nc) {
   return best;
 }
 
-template <int BN, int KIND, int STAGES>
+template <int BN, int KIND, int STAGES, bool OF8 = false>
 static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, const void* wq,
-                            const void* sw, int64_t M, int64_t N, int64_t Kb, void* y) {
+                            const void* sw, int64_t M, int64_t N, int64_t Kb, void* y,
+                            const Epilogue& ep = Epilogue{}) {
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int ksteps = (int)(Kb / 128);
-  const int vec = (N % 8) == 0;
-  hipLaunchKernelGGL((gemm_kernel<BN, KIND, STAGES>), dim3((unsigned)(tiles_m * tiles_n)),
+  // 16-byte row stores need 16-byte aligned rows: N % 8 == 0 for bf16, N % 16 for bytes.
+  const int vec = OF8 ? (N % 16) == 0 : (N % 8) == 0;
+  hipLaunchKernelGGL((gemm_kernel<BN, KIND, STAGES, OF8>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(kThreads), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
-                     (int)M, (int)N, (int)Kb, ksteps, (uint16_t*)y, tiles_m, vec);
+                     (int)M, (int)N, (int)Kb, ksteps, y, tiles_m, vec, ep);
   return hipGetLastError();
 }
 
@@ -400,24 +420,33 @@ static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, cons
 // block-scaled variant keeps a per-group partial and its scales in registers, so it
 // stops at 192; the scale-carrying variants use two stages so that one vmcnt(0) per step
 // also retires their scale loads.
-hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
-                       int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st) {
-  if (use_skinny(M, N)) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st);
+template <bool OF8>
+static hipError_t launch_scaled(const void* xq, const float* sx, const void* wq, const float* sw,
+                                int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                                const Epilogue& ep) {
   if (fmt == 1) {
     static const int c[3] = {256, 192, 128};
     switch (pick_bn(M, N, c, 3)) {
-      case 256: return launch_bn<256, KIND_INT8, 2>(st, xq, sx, wq, sw, M, N, K, y);
-      case 192: return launch_bn<192, KIND_INT8, 2>(st, xq, sx, wq, sw, M, N, K, y);
-      default: return launch_bn<128, KIND_INT8, 3>(st, xq, sx, wq, sw, M, N, K, y);
+      case 256: return launch_bn<256, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+      case 192: return launch_bn<192, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+      default: return launch_bn<128, KIND_INT8, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
     }
   }
   static const int c[4] = {256, 224, 192, 128};
   switch (pick_bn(M, N, c, 4)) {
-    case 256: return launch_bn<256, KIND_FP8, 2>(st, xq, sx, wq, sw, M, N, K, y);
-    case 224: return launch_bn<224, KIND_FP8, 2>(st, xq, sx, wq, sw, M, N, K, y);
-    case 192: return launch_bn<192, KIND_FP8, 2>(st, xq, sx, wq, sw, M, N, K, y);
-    default: return launch_bn<128, KIND_FP8, 3>(st, xq, sx, wq, sw, M, N, K, y);
+    case 256: return launch_bn<256, KIND_FP8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    case 224: return launch_bn<224, KIND_FP8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    case 192: return launch_bn<192, KIND_FP8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    default: return launch_bn<128, KIND_FP8, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
   }
+}
+
+hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
+                       int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                       const Epilogue& ep) {
+  if (use_skinny(M, N)) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  if (ep.out_fp8) return launch_scaled<true>(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  return launch_scaled<false>(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
 }
 
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,

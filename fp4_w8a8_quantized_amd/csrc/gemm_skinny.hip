@@ -30,11 +30,11 @@
 
 namespace w8a8 {
 
-template <int KIND, int MT, int WPB, int NW>
+template <int KIND, int MT, int WPB, int NW, bool OF8>
 __global__ void __launch_bounds__(WPB * 64)
 gemm_skinny_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                    const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
-                   int K, int ksteps, uint16_t* __restrict__ y) {
+                   int K, int ksteps, void* __restrict__ yp, Epilogue ep) {
   typedef typename std::conditional<KIND == 1, i32x4, f32x4>::type acc_t;
   __shared__ __attribute__((aligned(16))) acc_t red[WPB][NW][MT][64];
 
@@ -137,30 +137,54 @@ gemm_skinny_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     float v[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float swn = sw[min(n + r, N - 1)];
-      if constexpr (KIND == 1) v[r] = __fmul_rn(__fmul_rn((float)s[r], sm), swn);
+      const int nn = min(n + r, N - 1);
+      const float swn = sw[nn];
+      if constexpr (KIND == 1) v[r] = mul_rn(mul_rn((float)s[r], sm), swn);
       else v[r] = s[r] * (sm * swn);
+      if (ep.bias) v[r] = add_rn(v[r], bf16_lo(ep.bias[nn]));
+      v[r] = epi_activate(v[r], ep.act);
     }
-    uint16_t* yr = y + (size_t)m * N;
-    if ((N & 3) == 0) {
-      const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *reinterpret_cast<u32x2*>(yr + n) = o;
-    } else {
-      const uint32_t o[2] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    if constexpr (OF8) {
+      constexpr bool EX = (KIND == 1);
+      const uint32_t o = pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
+                                     epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
+      uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + (size_t)m * N;
+      if ((N & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(yr + n) = o;
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (n + r < N) yr[n + r] = (uint16_t)((o[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) yr[n + r] = (uint8_t)((o >> (8 * r)) & 0xFFu);
+      }
+    } else {
+      uint16_t* yr = reinterpret_cast<uint16_t*>(yp) + (size_t)m * N;
+      if ((N & 3) == 0) {
+        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(yr + n) = o;
+      } else {
+        const uint32_t o[2] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (n + r < N) yr[n + r] = (uint16_t)((o[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+      }
     }
   }
 }
 
 template <int KIND, int MT, int WPB, int NW>
 static hipError_t launch_cfg(const void* xq, const float* sx, const void* wq, const float* sw,
-                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
+                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                             const Epilogue& ep) {
   const int blocks = (int)((N + 16 * NW - 1) / (16 * NW));
-  hipLaunchKernelGGL((gemm_skinny_kernel<KIND, MT, WPB, NW>), dim3((unsigned)blocks), dim3(WPB * 64),
-                     0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw, (int)M, (int)N,
-                     (int)K, (int)(K / 128), (uint16_t*)y);
+  if (ep.out_fp8) {
+    hipLaunchKernelGGL((gemm_skinny_kernel<KIND, MT, WPB, NW, true>), dim3((unsigned)blocks),
+                       dim3(WPB * 64), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
+                       (int)M, (int)N, (int)K, (int)(K / 128), y, ep);
+  } else {
+    hipLaunchKernelGGL((gemm_skinny_kernel<KIND, MT, WPB, NW, false>), dim3((unsigned)blocks),
+                       dim3(WPB * 64), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
+                       (int)M, (int)N, (int)K, (int)(K / 128), y, ep);
+  }
   return hipGetLastError();
 }
 
@@ -170,27 +194,29 @@ static hipError_t launch_cfg(const void* xq, const float* sx, const void* wq, co
 // N = 4096). Chosen from a sweep on MI355X at K = 4096, N in {4096, 14336}.
 template <int KIND>
 static hipError_t launch_kind(const void* xq, const float* sx, const void* wq, const float* sw,
-                              int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
+                              int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                              const Epilogue& ep) {
   const bool wide = N > 8192;
   if (M <= 16) {
-    return wide ? launch_cfg<KIND, 1, 8, 2>(xq, sx, wq, sw, M, N, K, y, st)
-                : launch_cfg<KIND, 1, 8, 1>(xq, sx, wq, sw, M, N, K, y, st);
+    return wide ? launch_cfg<KIND, 1, 8, 2>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                : launch_cfg<KIND, 1, 8, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
   }
   if (M <= 32) {
-    return wide ? launch_cfg<KIND, 2, 4, 4>(xq, sx, wq, sw, M, N, K, y, st)
-                : launch_cfg<KIND, 2, 8, 1>(xq, sx, wq, sw, M, N, K, y, st);
+    return wide ? launch_cfg<KIND, 2, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                : launch_cfg<KIND, 2, 8, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
   }
   if (M <= 64) {
-    return wide ? launch_cfg<KIND, 4, 4, 4>(xq, sx, wq, sw, M, N, K, y, st)
-                : launch_cfg<KIND, 4, 4, 1>(xq, sx, wq, sw, M, N, K, y, st);
+    return wide ? launch_cfg<KIND, 4, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                : launch_cfg<KIND, 4, 4, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
   }
-  return launch_cfg<KIND, 8, 4, 1>(xq, sx, wq, sw, M, N, K, y, st);   // M <= 128, N <= 8192
+  return launch_cfg<KIND, 8, 4, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);   // M <= 128, N <= 8192
 }
 
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
-                              int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st) {
-  if (fmt == 1) return launch_kind<1>(xq, sx, wq, sw, M, N, K, y, st);
-  return launch_kind<0>(xq, sx, wq, sw, M, N, K, y, st);
+                              int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                              const Epilogue& ep) {
+  if (fmt == 1) return launch_kind<1>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return launch_kind<0>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 }  // namespace w8a8

@@ -16,15 +16,28 @@ hipError_t launch_quantize_block(const void* w, int64_t N, int64_t K, void* q, f
 hipError_t launch_quantize_mxfp4(const void* x, int64_t R, int64_t K, void* q, uint8_t* sc,
                                  hipStream_t st);
 
+// What the GEMM epilogue does after dequantization: add a bf16 bias (when non-null), apply
+// an activation (0 none, 1 ReLU, 2 SiLU), and store bf16 or, when out_fp8, E4M3FN codes
+// of clamp(v / s_out, +-448). The default is the plain bf16 epilogue.
+struct Epilogue {
+  const uint16_t* bias = nullptr;
+  int act = 0;
+  int out_fp8 = 0;
+  float s_out = 1.f;
+  float inv_s_out = 1.f;            // fp32(1 / s_out)
+};
+
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
-                       int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st);
+                       int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                       const Epilogue& ep = Epilogue{});
 // Few-token form of launch_gemm: weights streamed by 16-, 32- or 64-row workgroups that
 // split K among their waves. It wins while the weights dominate the traffic: up to 64
 // tokens, and up to 128 on layers of at most 8192 outputs (measured crossover against the
 // tiled kernel at K = 4096).
 inline bool use_skinny(int64_t M, int64_t N) { return M <= 64 || (M <= 128 && N <= 8192); }
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
-                              int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st);
+                              int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                              const Epilogue& ep);
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                    hipStream_t st);

@@ -94,6 +94,39 @@ w8a8_status w8a8_quantize_weight_per_channel(const void* w_bf16, int64_t N, int6
 w8a8_status w8a8_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                       int64_t M, int64_t N, int64_t K, int fmt, void* y_bf16, void* stream);
 
+typedef enum {
+  W8A8_ACT_NONE = 0,        /* identity                                                */
+  W8A8_ACT_RELU = 1,        /* max(v, 0)                                               */
+  W8A8_ACT_SILU = 2         /* v * sigmoid(v) = v / (1 + exp(-v))                      */
+} w8a8_activation;
+
+typedef enum {
+  W8A8_OUT_BF16 = 0,        /* bf16 [M, N]                                             */
+  W8A8_OUT_E4M3FN = 1       /* E4M3FN bytes [M, N], requantized with a static scale    */
+} w8a8_output;
+
+/* ------------------------------------------------------------------------------------
+ * W8A8 GEMM with the whole epilogue of [P-FP8INT8] §6-9 ("Under the hood", the FP8 GEMM
+ * epilogue), for the next layer's input:
+ *   v = the dequantized sum of w8a8_gemm (same arithmetic, before its bf16 rounding)
+ *   v = v + bias[n]                 if bias_bf16 != NULL (bf16 [N], widened exactly)
+ *   v = act(v)                      act is a w8a8_activation
+ *   BF16 output:    y[m,n] = bf16_rne(v)                                    y: bf16 [M, N]
+ *   E4M3FN output:  y[m,n] = e4m3_rne(clamp(v / out_scale, -448, 448))      y: bytes [M, N]
+ * With INT8 operands v is fp32(fp32(fp32(acc) s_x[m]) s_w[n]), the bias add is one fp32
+ * addition and the division an IEEE fp32 division, so the outputs are bit-exact for
+ * W8A8_ACT_NONE and W8A8_ACT_RELU. With E4M3FN operands (whose sums are order-free) the
+ * division is a product with fp32(1 / out_scale). SiLU uses the hardware exponential and
+ * reciprocal.
+ * out_scale (the static per-tensor scale of the next layer's input) must be finite and
+ * > 0 for E4M3FN output and is ignored for BF16. A bad act, out_fmt or fmt returns
+ * W8A8_ERR_UNSUPPORTED, a bad out_scale W8A8_ERR_ARG; other rules as w8a8_gemm.
+ * bias_bf16, when given, is a 16-byte aligned device array of N bf16 values.
+ */
+w8a8_status w8a8_gemm_ex(const void* xq, const float* sx, const void* wq, const float* sw,
+                         int64_t M, int64_t N, int64_t K, int fmt, const void* bias_bf16,
+                         int act, int out_fmt, float out_scale, void* y, void* stream);
+
 /* ------------------------------------------------------------------------------------
  * DeepSeek-V3-style fine-grained FP8 ([P-FP8INT8] §5 "What DeepSeek did" and "The
  * blockwise/fine-grained trend"; [P-FP8FP4] "Scale granularity").

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["w8a8_quantize_per_token", "w8a8_quantize_weight_per_channel", "w8a8_gemm",
+    for n in ["w8a8_quantize_per_token", "w8a8_quantize_weight_per_channel", "w8a8_gemm", "w8a8_gemm_ex",
               "w8a8_quantize_per_token_group", "w8a8_quantize_weight_block", "w8a8_gemm_blockscaled",
               "w8a8_quantize_mxfp4", "w8a8_gemm_mxfp4", "w8a8_channel_absmax",
               "w8a8_smoothquant_scales", "w8a8_smooth_apply", "w8a8_status_string"]:
@@ -85,6 +85,22 @@ def test_gemm_validation(L):
     assert g(A, A, A, A, 4, 4, 128, 0, MIS, None) == EALIGN
     assert g(None, None, None, None, 0, 4, 128, 0, None, None) == OK
     assert g(None, None, None, None, 4, 0, 128, 1, None, None) == OK
+
+
+def test_gemm_ex_validation(L):
+    g = L.w8a8_gemm_ex
+    ok_args = (A, A, A, A, 4, 4, 128, 0)
+    assert g(*ok_args, None, 3, 0, 1.0, A, None) == EUNSUP              # activation
+    assert g(*ok_args, None, 0, 2, 1.0, A, None) == EUNSUP              # output format
+    assert g(*ok_args[:7], 5, None, 0, 0, 1.0, A, None) == EUNSUP        # operand format
+    assert g(*ok_args, None, 0, 1, 0.0, A, None) == EARG                # out_scale <= 0
+    assert g(*ok_args, None, 0, 1, -2.0, A, None) == EARG
+    assert g(*ok_args, None, 0, 1, float("nan"), A, None) == EARG
+    assert g(*ok_args, None, 0, 1, float("inf"), A, None) == EARG
+    assert g(*ok_args, MIS, 1, 0, 1.0, A, None) == EALIGN               # bias alignment
+    assert g(A, A, A, A, 4, 4, 100, 0, None, 0, 0, 1.0, A, None) == EUNSUP   # K % 128
+    assert g(A, A, A, A, 4, 4, 128, 0, None, 0, 0, 1.0, None, None) == ENULL
+    assert g(None, None, None, None, 0, 4, 128, 0, None, 2, 1, 1.0, None, None) == OK
 
 
 def test_blockscaled_validation(L):
