@@ -26,8 +26,10 @@ Pinning status (what each part is checked against lives in ``tests/test_oracle_*
 * roofline.py     pinned (numbers printed on [P-FP8FP4] and [P-LOWBIT] §5)
 * epilogue.py     pinned (options off = the plain references; SiLU closed forms and an
                   independent routine; hand-computed INT8 order and FP8-code examples)
+* static_scale.py pinned (one row at its own amax scale = the dynamic quantizer; hand
+                  saturation counts; a worked delayed-scaling window)
 """
 
-from . import formats, quant, gemm, smoothquant, roofline, epilogue  # noqa: F401
+from . import formats, quant, gemm, smoothquant, roofline, epilogue, static_scale  # noqa: F401
 
-__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue"]
+__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue", "static_scale"]
