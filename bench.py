@@ -21,6 +21,9 @@ Other workloads (`--workload decode|blockscaled|mxfp4|all`) print one JSON line 
   epilogue     the prefill linears with the full epilogue: + bf16 bias, SiLU, and FP8
                output requantized with a static scale (calibrated once, untimed), against
                the plain bf16 epilogue on the same inputs.
+  static       static per-tensor FP8 quantization with the saturation counter and running
+               amax, against the dynamic per-token quantizer, on the prefill activations
+               (2048 x 4096 and 2048 x 14336).
 """
 
 from __future__ import annotations
@@ -51,7 +54,7 @@ def _parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "blockscaled", "mxfp4", "epilogue", "all"])
+                   choices=["prefill", "decode", "blockscaled", "mxfp4", "epilogue", "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=256,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
@@ -379,6 +382,52 @@ def run_epilogue(args, c: Ctx):
     return rec
 
 
+# ----------------------------------------------------------------------------- static
+def run_static(args, c: Ctx):
+    """Static per-tensor quantize (+ saturation count + amax) vs dynamic per-token."""
+    import numpy as np
+    import synthetic
+    torch, L, sh = c.torch, c.L, c.sh
+    rows = []
+    for i in (0, 3):                                    # K = 4096 and K = 14336 activations
+        name, xb, _ = synthetic.prefill(i, n_limit=1)
+        x = c.bf16(xb)
+        M, K = x.shape
+        q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=c.dev)
+        sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
+        amax0 = float(x.float().abs().max())
+        scale = torch.tensor([amax0 / 448.0 / 2], dtype=torch.float32, device=c.dev)  # saturates the top
+        sat = torch.zeros((1,), dtype=torch.int32, device=c.dev)
+        amax = torch.zeros((1,), dtype=torch.float32, device=c.dev)
+
+        def dyn():
+            c.check(L.w8a8_quantize_per_token(x.data_ptr(), M, K, 0, q.data_ptr(), sx.data_ptr(), sh))
+
+        def sta():
+            c.check(L.w8a8_quantize_static(x.data_ptr(), M, K, 0, scale.data_ptr(), q.data_ptr(),
+                                           sat.data_ptr(), amax.data_ptr(), sh))
+
+        _, d_s, s_s = _timed_pair(args, c, dyn, sta)
+        byt = 3.0 * M * K
+        rows.append({"name": name, "M": M, "K": K, "dynamic_us": round(d_s * 1e6, 2),
+                     "static_us": round(s_s * 1e6, 2),
+                     "dynamic_GBps": round((byt + 4 * M) / d_s / 1e9, 1),
+                     "static_GBps": round(byt / s_s / 1e9, 1),
+                     "saturated_per_call": int(sat.item()) // (args.steps + args.warmup)})
+    tot_b = sum(3.0 * r["M"] * r["K"] for r in rows)
+    tot_s = sum(r["static_us"] for r in rows) * 1e-6
+    achieved = tot_b / tot_s / 1e9
+    rec = _base_record(args, "Static per-tensor FP8 quantize with saturation monitor, HBM GB/s",
+                       achieved, "GB/s", tot_s * 1e3, "fp8_e4m3fn",
+                       {"workload": "prefill activations 2048x4096 and 2048x14336, one static scale "
+                                    "(set to half the tensor amax / 448, so the top values saturate), "
+                                    "saturation counter and running amax on"})
+    rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    rec["cases"] = rows
+    return rec
+
+
 # ----------------------------------------------------------------------------- decode
 def decode_cpu_baseline():
     """Oracle on the M = 8, N = 4096 decode case, FP8 path (quantize + fp64 contraction)."""
@@ -618,7 +667,7 @@ def main():
         return
     c = Ctx()
     runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
-            "epilogue": run_epilogue,
+            "epilogue": run_epilogue, "static": run_static,
             "mxfp4": run_mxfp4}
     names = list(runs) if args.workload == "all" else [args.workload]
     for name in names:

@@ -21,6 +21,7 @@ import torch
 __all__ = [
     "lib", "library_path", "status_string", "W8A8Error",
     "quantize_per_token", "quantize_weight_per_channel", "gemm", "gemm_ex", "linear",
+    "quantize_static", "delayed_scale_update",
     "quantize_per_token_group", "quantize_weight_block", "gemm_blockscaled",
     "quantize_mxfp4", "gemm_mxfp4",
     "channel_absmax", "smoothquant_scales", "smooth_apply",
@@ -45,6 +46,8 @@ _SIGNATURES = {
     "w8a8_gemm": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp],
     "w8a8_gemm_ex": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
                      _c_int, _c_float, _c_vp, _c_vp],
+    "w8a8_quantize_static": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp],
+    "w8a8_delayed_scale_update": [_c_vp, _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_vp],
     "w8a8_quantize_per_token_group": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "w8a8_quantize_weight_block": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
@@ -207,6 +210,41 @@ def linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor) -> torch.Tensor:
     fmt = FMT_INT8 if wq.dtype == torch.int8 else FMT_E4M3FN
     xq, sx = quantize_per_token(x, fmt)
     return gemm(xq, sx, wq, sw)
+
+
+# ------------------------------------------------------------------------------ static scales
+def quantize_static(x: torch.Tensor, scale: torch.Tensor, fmt="e4m3fn",
+                    saturated: torch.Tensor | None = None, amax: torch.Tensor | None = None):
+    """X bf16 [M, K] with one static scale (fp32 tensor of one element, on the GPU) ->
+    codes [M, K]. `saturated` (int32/uint32, one element) accumulates the number of
+    clipped elements; `amax` (fp32, one element, >= 0) the running max |x|."""
+    f = _fmt(fmt)
+    _dev(x, "x", torch.bfloat16, 2)
+    for t, n, dt in ((scale, "scale", torch.float32), (saturated, "saturated", (torch.int32, torch.uint32)),
+                     (amax, "amax", torch.float32)):
+        if t is not None:
+            _dev(t, n, dt, t.dim())
+            if t.numel() < 1:
+                raise ValueError(f"{n} must hold one element")
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=_CODE_DTYPE[f], device=x.device)
+    _check(lib().w8a8_quantize_static(x.data_ptr(), M, K, f, scale.data_ptr(), q.data_ptr(),
+                                      saturated.data_ptr() if saturated is not None else None,
+                                      amax.data_ptr() if amax is not None else None, _stream(x)),
+           "w8a8_quantize_static")
+    return q
+
+
+def delayed_scale_update(history: torch.Tensor, amax: torch.Tensor, step: int, scale: torch.Tensor,
+                         fmt="e4m3fn") -> None:
+    """history[step % H] = amax; amax = 0; scale = max(max(history), 1e-8) / qmax (on the GPU)."""
+    f = _fmt(fmt)
+    _dev(history, "history", torch.float32, 1)
+    _dev(amax, "amax", torch.float32, amax.dim())
+    _dev(scale, "scale", torch.float32, scale.dim())
+    _check(lib().w8a8_delayed_scale_update(history.data_ptr(), history.numel(), amax.data_ptr(), int(step),
+                                           f, scale.data_ptr(), _stream(history)),
+           "w8a8_delayed_scale_update")
 
 
 # ------------------------------------------------------------------------------ block-scaled

@@ -14,6 +14,7 @@ namespace {
 constexpr int64_t kMaxOperandBytes = (int64_t)1 << 31;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 w8a8_status hip_status(hipError_t e) { return e == hipSuccess ? W8A8_OK : W8A8_ERR_HIP; }
 
@@ -103,6 +104,32 @@ w8a8_status w8a8_gemm_ex(const void* xq, const float* sx, const void* wq, const 
   const w8a8::Epilogue ep{reinterpret_cast<const uint16_t*>(bias_bf16), act,
                           out_fmt == W8A8_OUT_E4M3FN ? 1 : 0, out_scale, 1.f / out_scale};
   return hip_status(w8a8::launch_gemm(xq, sx, wq, sw, M, N, K, fmt, y, as_stream(stream), ep));
+}
+
+w8a8_status w8a8_quantize_static(const void* x_bf16, int64_t M, int64_t K, int fmt,
+                                 const float* scale, void* q, uint32_t* saturated,
+                                 float* amax, void* stream) {
+  if (fmt != W8A8_FMT_E4M3FN && fmt != W8A8_FMT_INT8) return W8A8_ERR_UNSUPPORTED;
+  w8a8_status st = check_dims(M, K);
+  if (st != W8A8_OK) return st;
+  if (K % 8 != 0) return W8A8_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return W8A8_OK;
+  if (!x_bf16 || !q || !scale) return W8A8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(q) || !aligned4(scale) || !aligned4(saturated) ||
+      !aligned4(amax))
+    return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_quantize_static(x_bf16, M, K, fmt, scale, q, saturated, amax,
+                                                 as_stream(stream)));
+}
+
+w8a8_status w8a8_delayed_scale_update(float* amax_history, int64_t H, float* amax, int64_t step,
+                                      int fmt, float* scale, void* stream) {
+  if (fmt != W8A8_FMT_E4M3FN && fmt != W8A8_FMT_INT8) return W8A8_ERR_UNSUPPORTED;
+  if (H < 1 || H > ((int64_t)1 << 24) || step < 0) return W8A8_ERR_ARG;
+  if (!amax_history || !amax || !scale) return W8A8_ERR_NULL;
+  if (!aligned4(amax_history) || !aligned4(amax) || !aligned4(scale)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_delayed_scale(amax_history, H, amax, step, fmt, scale,
+                                               as_stream(stream)));
 }
 
 w8a8_status w8a8_quantize_per_token_group(const void* x_bf16, int64_t M, int64_t K, void* xq,

@@ -50,6 +50,14 @@ __device__ __forceinline__ float div_by_scale(float x, float s, float rcp) {
   return __builtin_copysignf(__builtin_fmaf(r, rcp, q0), x);
 }
 
+// x / s for an arbitrary scale s in [2^-60, 2^60] (rcp = 1/s): the quotient above, except
+// that an overflowing first product is kept (an infinite quotient, which saturates,
+// instead of the NaN the correction would make of it).
+__device__ __forceinline__ float div_static(float x, float s, float rcp) {
+  const float q0 = __fmul_rn(x, rcp);
+  return __builtin_isfinite(q0) ? div_by_scale(x, s, rcp) : q0;
+}
+
 // Round to nearest even and clamp to [-127, 127], as a byte.
 __device__ __forceinline__ uint32_t int8_code(float v) {
   int i = (int)__builtin_rintf(v);       // v_rndne_f32 + v_cvt_i32_f32 (exact integer)

@@ -9,6 +9,10 @@ namespace w8a8 {
 
 hipError_t launch_quantize_rows(const void* x, int64_t R, int64_t K, int fmt, void* q,
                                 float* scale, hipStream_t st);
+hipError_t launch_quantize_static(const void* x, int64_t M, int64_t K, int fmt, const float* scale,
+                                  void* q, uint32_t* saturated, float* amax, hipStream_t st);
+hipError_t launch_delayed_scale(float* history, int64_t H, float* amax, int64_t step, int fmt,
+                                float* scale, hipStream_t st);
 hipError_t launch_quantize_group(const void* x, int64_t M, int64_t K, void* q, float* sx,
                                  hipStream_t st);
 hipError_t launch_quantize_block(const void* w, int64_t N, int64_t K, void* q, float* sw,

@@ -128,6 +128,37 @@ w8a8_status w8a8_gemm_ex(const void* xq, const float* sx, const void* wq, const 
                          int act, int out_fmt, float out_scale, void* y, void* stream);
 
 /* ------------------------------------------------------------------------------------
+ * Static per-tensor activation quantization with a saturation monitor ([P-FP8INT8] §5
+ * "FP8 in practice": x_fp8 = clamp(x / s, -448, 448); [P-FP8FP4] "Failure modes and how
+ * to detect them": log the fraction of saturated values per layer).
+ *   E4M3FN: q = e4m3_rne(clamp(x / s, -448, 448));  saturated if |x / s| > 448
+ *   INT8:   q = clamp(rne(x / s), +-127);            saturated if |rne(x / s)| > 127
+ * x / s is an IEEE fp32 division; s = scale[0] is read on the device (so that a scale
+ * produced by w8a8_delayed_scale_update needs no host round trip).
+ *   x_bf16 [M, K]; q [M, K] bytes; K % 8 == 0.
+ *   saturated (may be NULL): one uint32 to which the number of saturated elements is
+ *     added (atomically; the caller zeroes it when a new count should start).
+ *   amax (may be NULL): one float, set to max(amax, max |x|) (atomically; NaN elements
+ *     are ignored; it must hold a value >= 0 before the call).
+ * scale, saturated and amax need only 4-byte alignment. NaN elements encode to a NaN
+ * code (E4M3FN) or 0 (INT8) and are not counted.
+ */
+w8a8_status w8a8_quantize_static(const void* x_bf16, int64_t M, int64_t K, int fmt,
+                                 const float* scale, void* q, uint32_t* saturated,
+                                 float* amax, void* stream);
+
+/* Delayed scaling ([P-FP8INT8] §5 "FP8 in practice": the scale comes from a history of
+ * recent amax values, avoiding a synchronization). On the device, in stream order:
+ *   amax_history[step mod H] = *amax;  *amax = 0;
+ *   *scale = fp32(max(max_i amax_history[i], 1e-8)) / qmax     (qmax 448 or 127 by fmt)
+ * amax_history: float [H], 1 <= H <= 2^24, caller-initialised (e.g. with calibration
+ * amax values). Run once per step after w8a8_quantize_static; the next step's quantize
+ * then reads the new scale. All pointers 4-byte aligned device pointers; step >= 0.
+ */
+w8a8_status w8a8_delayed_scale_update(float* amax_history, int64_t H, float* amax, int64_t step,
+                                      int fmt, float* scale, void* stream);
+
+/* ------------------------------------------------------------------------------------
  * DeepSeek-V3-style fine-grained FP8 ([P-FP8INT8] §5 "What DeepSeek did" and "The
  * blockwise/fine-grained trend"; [P-FP8FP4] "Scale granularity").
  *

@@ -103,6 +103,28 @@ def test_gemm_ex_validation(L):
     assert g(None, None, None, None, 0, 4, 128, 0, None, 2, 1, 1.0, None, None) == OK
 
 
+def test_static_validation(L):
+    q = L.w8a8_quantize_static
+    assert q(A, 4, 64, 3, A, A, None, None, None) == EUNSUP             # format
+    assert q(A, 4, 60, 0, A, A, None, None, None) == EUNSUP             # K % 8
+    assert q(None, 4, 64, 0, A, A, None, None, None) == ENULL
+    assert q(A, 4, 64, 0, None, A, None, None, None) == ENULL           # scale
+    assert q(A, 4, 64, 0, A, None, None, None, None) == ENULL
+    assert q(MIS, 4, 64, 0, A, A, None, None, None) == EALIGN
+    assert q(A, 4, 64, 0, 0x10002, A, None, None, None) == EALIGN       # scale 2-byte aligned
+    assert q(A, 4, 64, 1, A, A, 0x10001, None, None) == EALIGN
+    assert q(A, -1, 64, 0, A, A, None, None, None) == ESHAPE
+    assert q(None, 0, 64, 0, None, None, None, None, None) == OK
+    d = L.w8a8_delayed_scale_update
+    assert d(A, 0, A, 0, 0, A, None) == EARG                            # H >= 1
+    assert d(A, 1 << 25, A, 0, 0, A, None) == EARG
+    assert d(A, 4, A, -1, 0, A, None) == EARG                           # step >= 0
+    assert d(A, 4, A, 0, 2, A, None) == EUNSUP
+    assert d(None, 4, A, 0, 0, A, None) == ENULL
+    assert d(A, 4, None, 0, 0, A, None) == ENULL
+    assert d(A, 4, A, 0, 0, 0x10002, None) == EALIGN
+
+
 def test_blockscaled_validation(L):
     assert L.w8a8_quantize_per_token_group(A, 4, 100, A, A, None) == EUNSUP
     assert L.w8a8_quantize_per_token_group(None, 4, 128, A, A, None) == ENULL
