@@ -45,7 +45,7 @@ FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_gemm_prefill_8b_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "fp4_w8a8_quantized_amd", "csrc", f)
-                for f in ("gemm.hip", "common.h")]
+                for f in ("gemm_pp.hip", "common.h")]
 
 
 def _parse_args():

@@ -415,38 +415,31 @@ static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, cons
   return hipGetLastError();
 }
 
-// Tile widths per variant. 16x16 variants: 256, 224, 192 (two LDS stages) and 128
-// (three stages: deeper prefetch fits in LDS). 32x32 variants need multiples of 64. The
+// Tile widths per variant. 32x32 variants (INT8, MXFP4) need multiples of 64. The
 // block-scaled variant keeps a per-group partial and its scales in registers, so it
 // stops at 192; the scale-carrying variants use two stages so that one vmcnt(0) per step
 // also retires their scale loads.
 template <bool OF8>
-static hipError_t launch_scaled(const void* xq, const float* sx, const void* wq, const float* sw,
-                                int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
-                                const Epilogue& ep) {
-  if (fmt == 1) {
-    static const int c[3] = {256, 192, 128};
-    switch (pick_bn(M, N, c, 3)) {
-      case 256: return launch_bn<256, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-      case 192: return launch_bn<192, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-      default: return launch_bn<128, KIND_INT8, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-    }
-  }
-  static const int c[4] = {256, 224, 192, 128};
-  switch (pick_bn(M, N, c, 4)) {
-    case 256: return launch_bn<256, KIND_FP8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-    case 224: return launch_bn<224, KIND_FP8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-    case 192: return launch_bn<192, KIND_FP8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-    default: return launch_bn<128, KIND_FP8, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+static hipError_t launch_int8(const void* xq, const float* sx, const void* wq, const float* sw,
+                              int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                              const Epilogue& ep) {
+  static const int c[3] = {256, 192, 128};
+  switch (pick_bn(M, N, c, 3)) {
+    case 256: return launch_bn<256, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    case 192: return launch_bn<192, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    default: return launch_bn<128, KIND_INT8, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
   }
 }
 
+// Few tokens: the weight-streaming kernel; FP8 otherwise: the two-waves-per-SIMD kernel;
+// INT8: the tiled kernel of this file.
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                        const Epilogue& ep) {
   if (use_skinny(M, N)) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
-  if (ep.out_fp8) return launch_scaled<true>(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
-  return launch_scaled<false>(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
+  if (ep.out_fp8) return launch_int8<true>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return launch_int8<false>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,

@@ -1,0 +1,299 @@
+// FP8 W8A8 GEMM on gfx950 with two waves per SIMD taking turns ("ping-pong"):
+//   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )     (v_mfma 16x16x128 f8f6f4)
+// with the scale factoring of "FP8 and FP4 inference, SmoothQuant and activation
+// quantization" (Scale granularity) and the epilogue of "FP8 and INT8 Inference" §6-9.
+//
+// Why two waves per SIMD. A wave issues in order: with one wave per SIMD, every LDS read
+// and every direct-to-LDS load it issues sits between two MFMAs, and the CU's address
+// unit (about 64 B per clock) and LDS latency hold back the matrix core. Here a 512-thread
+// workgroup (8 waves, 2 per SIMD) computes a 256 x BN tile; each wave owns 128 x BN/4 of
+// it. Waves 0-3 (group A) and 4-7 (group B) alternate between two phases separated by
+// workgroup barriers:
+//   LDS phase:  read this step's X and W fragments into registers
+//   MFMA phase: SM x SN MFMAs on them
+// so that while one wave of a SIMD issues memory instructions the other keeps the matrix
+// core busy. Slot 2k: A reads step k, B computes step k-1; slot 2k+1: A computes step k,
+// B reads step k.
+//
+// LDS: two stages of [256 x 128 B of X | BN x 128 B of W]. Group B reads a stage last,
+// so group B refills it, but only once all four B waves are done reading it: the odd slot
+// has a barrier in its middle (group A splits its MFMA phase around it). After that barrier
+// each B wave issues half of its loads of step k+2 into the stage, waits for its loads of
+// step k+1 (so the barrier that ends the slot publishes them to A), and issues the other
+// half between the MFMAs of its next phase. The stage is next read by A two slots later.
+//
+// Fragments: lane l reads row l & 15 and the 16-byte chunks g and g + 4 (g = l >> 4) of the
+// 128-byte K step; both operands permute K the same way, so every dot product still covers
+// the whole step. This assignment keeps the 8-wave fragment reads free of bank conflicts
+// (about twice the throughput of chunks 2g, 2g + 1 on gfx950's LDS). Rows sit 128 B apart
+// with chunk c at slot c ^ ((row >> 1) & 7).
+//
+// Epilogue: scale, bias, activation, convert (bf16, or E4M3FN of clamp(v / s_out)) in
+// registers, stage the tile through the freed LDS, write whole rows with 16-byte stores.
+#include "common.h"
+#include "internal.h"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kPPBM = 256;
+constexpr int kPPThreads = 512;
+
+__device__ __forceinline__ int pp_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// One 16-byte direct global->LDS load per lane (lane l writes LDS bytes [m0 + 16 l, +16)).
+// M0 is written by the same inline assembly, with the one wait state gfx9 asks for
+// between an SALU write of M0 and an LDS-DMA that reads it.
+__device__ __forceinline__ void pp_dma16(uint32_t lds_addr, uint32_t voff, const uint8_t* gbase) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory");
+}
+
+// s_waitcnt immediate (gfx9: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14).
+constexpr int pp_wait(int vm, int lgkm) {
+  return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | (((vm >> 4) & 3) << 14);
+}
+
+__device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int BN, bool OF8>
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
+               const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
+               int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
+  constexpr int BM = kPPBM;
+  constexpr int SM = 8;                       // 128 rows per wave, 16-row subtiles
+  constexpr int WC = BN / 4;                  // columns per wave
+  constexpr int SN = WC / 16;
+  static_assert(SN * 16 * 4 == BN, "tile width must give whole 16-column subtiles per wave");
+  constexpr int XT = BM * 128, WT = BN * 128, STAGE = XT + WT;
+  constexpr int XI = BM / 32, WI = BN / 32;   // 1 KB loads per group-B wave per step
+  constexpr int DMA = XI + WI;
+  constexpr int DC = DMA / 2;                 // of which issued during the MFMA phase
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int grp = wave >> 2, g4 = wave & 3;
+  const int wm = g4 & 1, wn = grp * 2 + (g4 >> 1);
+  // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that consecutive tiles
+  // (which share a W panel) run on one XCD and its L2.
+  int b = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  const int tm = b % tiles_m, tn = b / tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+  // Load d of a step (group B): d < XI fills X rows 8 (g4 + 4 d) .. +7, else W rows; lane l
+  // fetches chunk (l & 7) ^ swizzle of row 8q + (l >> 3) into its slot. Rows past M or N
+  // re-read the last valid row (their results are never stored).
+  auto dma_one = [&](int ks, int stage, int d) {
+    const uint32_t sbase = lds0 + stage * STAGE + g4 * 1024;
+    const bool isx = d < XI;
+    const int i = isx ? d : d - XI;
+    const int r = 8 * (g4 + 4 * i) + (lane >> 3);
+    const int row = isx ? min(m0 + r, M - 1) : min(n0 + r, N - 1);
+    const uint32_t vo = (uint32_t)row * (uint32_t)Kb + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    pp_dma16(sbase + (isx ? 0 : XT) + i * 4096, vo, (isx ? xq : wq) + (size_t)ks * 128);
+  };
+
+  const int fr = lane & 15, g = lane >> 4;
+  const int fo0 = pp_off(fr, g), fo1 = pp_off(fr, g + 4);
+  const int xrow0 = wm * 128, wrow0 = wn * WC;
+  typedef int frag_t __attribute__((ext_vector_type(8)));
+  auto frag = [&](const uint8_t* base) -> frag_t {
+    const i32x4 a = *reinterpret_cast<const i32x4*>(base + fo0);
+    const i32x4 c = *reinterpret_cast<const i32x4*>(base + fo1);
+    return frag_t{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  };
+
+  f32x4 acc[SN][SM];
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+#pragma unroll
+    for (int i = 0; i < SM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  frag_t xf[SM], wf[SN];
+
+  auto lds_phase = [&](int ks) {
+    const uint8_t* X = lds + (ks & 1) * STAGE;
+    const uint8_t* W = X + XT;
+#pragma unroll
+    for (int i = 0; i < SM; ++i) xf[i] = frag(X + (xrow0 + 16 * i) * 128);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) wf[j] = frag(W + (wrow0 + 16 * j) * 128);
+    __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));      // this wave's reads of the stage done
+  };
+  constexpr int T = SM * SN;
+  // MFMAs number lo .. hi-1 of a step (row-major over the SM x SN subtiles).
+  auto mfma_range = [&](int lo, int hi) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+        if (i * SN + j >= lo && i * SN + j < hi)
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+  };
+  // Group B's MFMA phase, with the last DC loads of step kd between the MFMAs.
+  auto mfma_phase_loading = [&](int kd, int stage) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+        const int tt = i * SN + j;
+#pragma unroll
+        for (int d = 0; d < DC; ++d)
+          if (tt == (d * T) / DC) dma_one(kd, stage, DMA - DC + d);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+
+  // Prologue: group B loads steps 0 and 1; step 0 landed and published. Past the last
+  // step, loads re-fetch the last step into a stage nobody reads again (branch-free).
+  if (grp == 1) {
+#pragma unroll
+    for (int d = 0; d < DMA; ++d) dma_one(0, 0, d);
+#pragma unroll
+    for (int d = 0; d < DMA; ++d) dma_one(min(1, ksteps - 1), 1, d);
+    __builtin_amdgcn_s_waitcnt(pp_wait(DMA, 15));
+  }
+  pp_barrier();
+  // Both groups pass 3 * ksteps + 1 barriers in the loop part.
+  if (grp == 0) {
+    for (int ks = 0; ks < ksteps; ++ks) {
+      lds_phase(ks);                                   // slot 2k
+      __builtin_amdgcn_sched_barrier(0);
+      pp_barrier();
+      mfma_range(0, T / 2);                            // slot 2k+1, first half
+      __builtin_amdgcn_sched_barrier(0);
+      pp_barrier();
+      mfma_range(T / 2, T);                            // second half
+      __builtin_amdgcn_sched_barrier(0);
+      pp_barrier();
+    }
+    pp_barrier();
+  } else {
+    pp_barrier();                                      // slot 0
+    for (int ks = 0; ks < ksteps; ++ks) {
+      lds_phase(ks);                                   // slot 2k+1, first half
+      __builtin_amdgcn_sched_barrier(0);
+      pp_barrier();                                    // no wave reads stage ks & 1 any more
+      const int kd = min(ks + 2, ksteps - 1);
+#pragma unroll
+      for (int d = 0; d < DMA - DC; ++d) dma_one(kd, ks & 1, d);
+      // Everything older than this slot's loads has landed: that is all of step k+1.
+      __builtin_amdgcn_s_waitcnt(pp_wait(DMA - DC, 15));
+      __builtin_amdgcn_sched_barrier(0);
+      pp_barrier();
+      mfma_phase_loading(kd, ks & 1);                  // slot 2k+2
+      __builtin_amdgcn_sched_barrier(0);
+      pp_barrier();
+    }
+  }
+
+  // ---- epilogue. Every load has landed and every wave is past its last fragment read.
+  constexpr int ES = OF8 ? 1 : 2;                      // output bytes per element
+  constexpr bool SWZ = (BN == 256 && !OF8);
+  constexpr int RS = SWZ ? 512 : BN * ES + 16;         // padded rows: conflict-free column writes
+  static_assert(BM * RS <= 2 * STAGE, "output tile must fit in the pipeline LDS");
+  auto opos = [&](int row, int byte) -> int {
+    return SWZ ? row * RS + ((((byte >> 4) ^ (row & 15)) << 4) | (byte & 15)) : row * RS + byte;
+  };
+  float esm[SM], esn[SN][4], ebias[SN][4];
+  const bool has_bias = ep.bias != nullptr;
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1);
+      esn[j][r] = sw[n];
+      ebias[j][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
+    }
+#pragma unroll
+  for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + 16 * i + fr, M - 1)];
+  __builtin_amdgcn_s_waitcnt(pp_wait(0, 0));
+  pp_barrier();
+  // In the 16x16 result (A = W fragment, B = X fragment), lane l holds output row
+  // m = 16 i + (l & 15) and the four consecutive columns 16 j + 4 (l >> 4) + r.
+#pragma unroll
+  for (int i = 0; i < SM; ++i) {
+    const int rl = xrow0 + 16 * i + fr;
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int cl = wrow0 + 16 * j + 4 * g;
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[j][i][r] * (esm[i] * esn[j][r]);
+        if (has_bias) v[r] = add_rn(v[r], ebias[j][r]);
+        v[r] = epi_activate(v[r], ep.act);
+      }
+      if constexpr (OF8) {
+        *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
+            pack_e4m3x4(epi_requant<false>(v[0], ep.s_out, ep.inv_s_out), epi_requant<false>(v[1], ep.s_out, ep.inv_s_out),
+                        epi_requant<false>(v[2], ep.s_out, ep.inv_s_out), epi_requant<false>(v[3], ep.s_out, ep.inv_s_out));
+      } else {
+        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));
+  pp_barrier();
+  constexpr int EPC = 16 / ES;                         // output elements per 16-byte chunk
+  constexpr int CPR = BN / EPC;                        // chunks per output row
+  for (int c = t; c < BM * CPR; c += kPPThreads) {
+    const int rl = c / CPR, ch = c - rl * CPR;
+    const int m = m0 + rl, n = n0 + ch * EPC;
+    if (m >= M || n >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + opos(rl, ch * 16));
+    uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + ((size_t)m * N + n) * ES;
+    if (vec_store && n + EPC - 1 < N) {
+      *reinterpret_cast<u32x4*>(yr) = v;
+    } else {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        if (n + e >= N) break;
+        if constexpr (OF8) yr[e] = (uint8_t)((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+        else reinterpret_cast<uint16_t*>(yr)[e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      }
+    }
+  }
+}
+
+template <int BN, bool OF8>
+hipError_t launch_pp(const void* xq, const float* sx, const void* wq, const float* sw, int64_t M,
+                     int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
+  const int tiles_m = (int)((M + kPPBM - 1) / kPPBM);
+  const int tiles_n = (int)((N + BN - 1) / BN);
+  const int vec = OF8 ? (N % 16) == 0 : (N % 8) == 0;
+  hipLaunchKernelGGL((gemm_pp_kernel<BN, OF8>), dim3((unsigned)(tiles_m * tiles_n)),
+                     dim3(kPPThreads), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
+                     (int)M, (int)N, (int)K, (int)(K / 128), y, tiles_m, vec, ep);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile width: the one whose waves of workgroups over the 256 CUs cost least, weighting
+// each width by its measured steady-state MFMA efficiency (0.80 at 192, 0.66 at 128 on
+// MI355X: the wider tile spends a smaller share of each step on loads and barriers).
+hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const float* sw,
+                          int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                          const Epilogue& ep) {
+  const int64_t tm = (M + kPPBM - 1) / kPPBM;
+  const int64_t waves192 = (tm * ((N + 191) / 192) + 255) / 256;
+  const int64_t waves128 = (tm * ((N + 127) / 128) + 255) / 256;
+  const bool wide = waves192 * 240 <= waves128 * 194;   // 192 / 0.80 vs 128 / 0.66
+  if (ep.out_fp8)
+    return wide ? launch_pp<192, true>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                : launch_pp<128, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return wide ? launch_pp<192, false>(xq, sx, wq, sw, M, N, K, y, st, ep)
+              : launch_pp<128, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+}
+
+}  // namespace w8a8

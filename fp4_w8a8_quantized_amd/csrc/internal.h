@@ -34,6 +34,12 @@ struct Epilogue {
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                        const Epilogue& ep = Epilogue{});
+// FP8 form of launch_gemm for more tokens than the few-token kernel takes: 8 waves per
+// workgroup, two per SIMD alternating between LDS reads and MFMAs.
+hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const float* sw,
+                          int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                          const Epilogue& ep);
+
 // Few-token form of launch_gemm: weights streamed by 16-, 32- or 64-row workgroups that
 // split K among their waves. It wins while the weights dominate the traffic: up to 64
 // tokens, and up to 128 on layers of at most 8192 outputs (measured crossover against the

@@ -82,6 +82,28 @@ def test_fp8_few_tokens(M, N, K):
     _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
 
 
+# Regression: the two-waves-per-SIMD kernel refills an LDS stage while other waves of the
+# workgroup compute. A refill that starts before every wave has read the stage changes
+# results from run to run, so the same launch is repeated and must give identical bits.
+@pytest.mark.parametrize("M,N,K", [(256, 8193, 640), (2048, 4096, 1024), (512, 6144, 4096)])
+def test_fp8_repeat_identical(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, M + N + K)
+    xq, sx = w8.quantize_per_token(to_dev_bf16(xb))
+    wq, sw = w8.quantize_weight_per_channel(to_dev_bf16(wb))
+    y0 = w8.gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    ref = y0.clone()
+    for r in range(12):
+        w8.gemm(xq, sx, wq, sw, out=y0)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), ref.view(torch.int16)), f"{M}x{N}x{K}: run {r + 1} differs"
+    oxq, osx = Q.quantize_per_token_fp8(xb)
+    owq, osw = Q.quantize_weight_per_channel_fp8(wb)
+    rows = np.arange(0, M, max(1, M // 64))
+    _assert_tol(bf16_to_f64(ref)[rows], G.gemm_fp8_ref(oxq[rows], osx[rows], owq, osw), f"{M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("i", [0, 1, 2, 3])
 def test_fp8_prefill_full_size_sampled(i):
     """The 8B prefill linears at full size, in the bench's launch configuration; codes of
