@@ -121,7 +121,7 @@ def traffic_summary(args):
         return float(np.median(v)) if v else float("nan")
 
     def gemm_kib(path):
-        v = [x for n, x in _counter_rows(path) if "gemm_kernel" in n]
+        v = [x for n, x in _counter_rows(path) if "gemm_pp_kernel" in n]
         return float(np.mean(v)), len(v)
 
     f_scale = copy_bytes / (copy_kib(cf) * 1024.0)
@@ -644,7 +644,7 @@ def run_mxfp4(args, c: Ctx):
 def main():
     args = _parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
               "multi-GPU path: the method shards along tokens or output channels with no "
               "exchange, so the per-GPU kernel is what is measured.", file=sys.stderr)
         sys.exit(2)
