@@ -1,4 +1,4 @@
-"""CPU oracle for the W8A8 / block-scaled FP8 / SmoothQuant INT8 / MXFP4 hot path.
+"""CPU oracle for the W8A8 / block-scaled FP8 / SmoothQuant INT8 / MXFP4 / NVFP4 hot path.
 
 TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or link this
 package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -28,8 +28,11 @@ Pinning status (what each part is checked against lives in ``tests/test_oracle_*
                   independent routine; hand-computed INT8 order and FP8-code examples)
 * static_scale.py pinned (one row at its own amax scale = the dynamic quantizer; hand
                   saturation counts; a worked delayed-scaling window)
+* nvfp4.py        pinned (hand-computed grid blocks and scale codes, nearest-value brute
+                  force, the zero-scale rule, 4.5 bits per element from [P-LOWBIT] §2.4,
+                  triple-loop GEMM)
 """
 
-from . import formats, quant, gemm, smoothquant, roofline, epilogue, static_scale  # noqa: F401
+from . import formats, quant, gemm, smoothquant, roofline, epilogue, static_scale, nvfp4  # noqa: F401
 
-__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue", "static_scale"]
+__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue", "static_scale", "nvfp4"]
