@@ -53,6 +53,8 @@ _SIGNATURES = {
     "w8a8_gemm_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
     "w8a8_quantize_mxfp4": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm_mxfp4": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
+    "w8a8_quantize_nvfp4": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp],
+    "w8a8_gemm_nvfp4": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
     "w8a8_channel_absmax": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp],
     "w8a8_smoothquant_scales": [_c_vp, _c_vp, _c_i64, _c_float, _c_vp, _c_vp],
     "w8a8_smooth_apply": [_c_vp, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_vp],
@@ -314,6 +316,47 @@ def gemm_mxfp4(xq, sx, wq, sw, out=None) -> torch.Tensor:
     _dev(y, "out", torch.bfloat16, 2)
     _check(lib().w8a8_gemm_mxfp4(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(),
                                  M, N, K, y.data_ptr(), _stream(xq)), "w8a8_gemm_mxfp4")
+    return y
+
+
+# ------------------------------------------------------------------------------ NVFP4
+NVFP4_SCALE_COMPUTE, NVFP4_SCALE_GIVEN = 0, 1
+
+
+def quantize_nvfp4(x: torch.Tensor, g: torch.Tensor | None = None):
+    """bf16 [R, K] -> (packed E2M1 uint8 [R, K/2], E4M3 scale codes uint8 [R, K/16],
+    tensor scale g fp32 [1]). With g None, g = amax / 2688 is computed from x; otherwise
+    the given fp32 [1] device tensor is used (and returned)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    R, K = x.shape
+    q = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((R, K // 16), dtype=torch.uint8, device=x.device)
+    if g is None:
+        g_out, mode = torch.empty((1,), dtype=torch.float32, device=x.device), NVFP4_SCALE_COMPUTE
+    else:
+        _dev(g, "g", torch.float32, 1)
+        g_out, mode = g, NVFP4_SCALE_GIVEN
+    _check(lib().w8a8_quantize_nvfp4(x.data_ptr(), R, K, mode, q.data_ptr(), s.data_ptr(),
+                                     g_out.data_ptr(), _stream(x)), "w8a8_quantize_nvfp4")
+    return q, s, g_out
+
+
+def gemm_nvfp4(xq, sx, gx, wq, sw, gw, out=None) -> torch.Tensor:
+    """y bf16 [M, N] from NVFP4 operands (packed codes, E4M3 scales per 16, fp32 g each)."""
+    for t, n in ((xq, "xq"), (wq, "wq"), (sx, "sx"), (sw, "sw")):
+        _dev(t, n, torch.uint8, 2)
+    _dev(gx, "gx", torch.float32, 1)
+    _dev(gw, "gw", torch.float32, 1)
+    M, Kh = xq.shape
+    N = wq.shape[0]
+    K = 2 * Kh
+    if wq.shape[1] != Kh or tuple(sx.shape) != (M, K // 16) or tuple(sw.shape) != (N, K // 16):
+        raise ValueError("NVFP4 operand shapes disagree")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _dev(y, "out", torch.bfloat16, 2)
+    _check(lib().w8a8_gemm_nvfp4(xq.data_ptr(), sx.data_ptr(), gx.data_ptr(), wq.data_ptr(),
+                                 sw.data_ptr(), gw.data_ptr(), M, N, K, y.data_ptr(), _stream(xq)),
+           "w8a8_gemm_nvfp4")
     return y
 
 

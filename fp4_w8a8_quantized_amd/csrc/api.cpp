@@ -183,6 +183,32 @@ w8a8_status w8a8_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq, c
   return hip_status(w8a8::launch_gemm_mxfp4(xq, sx, wq, sw, M, N, K, y_bf16, as_stream(stream)));
 }
 
+w8a8_status w8a8_quantize_nvfp4(const void* x_bf16, int64_t R, int64_t K, int scale_mode,
+                                void* q_packed, uint8_t* scale_e4m3, float* g, void* stream) {
+  if (scale_mode != W8A8_NVFP4_SCALE_COMPUTE && scale_mode != W8A8_NVFP4_SCALE_GIVEN)
+    return W8A8_ERR_UNSUPPORTED;
+  w8a8_status st = check_dims(R, K);
+  if (st != W8A8_OK) return st;
+  if (K % 16 != 0) return W8A8_ERR_UNSUPPORTED;
+  if (R == 0 || K == 0) return W8A8_OK;
+  if (!x_bf16 || !q_packed || !scale_e4m3 || !g) return W8A8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(q_packed) || !aligned16(scale_e4m3) || !aligned4(g))
+    return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_quantize_nvfp4(x_bf16, R, K, scale_mode == W8A8_NVFP4_SCALE_GIVEN,
+                                                q_packed, scale_e4m3, g, as_stream(stream)));
+}
+
+w8a8_status w8a8_gemm_nvfp4(const void* xq, const uint8_t* sx, const float* gx, const void* wq,
+                            const uint8_t* sw, const float* gw, int64_t M, int64_t N, int64_t K,
+                            void* y_bf16, void* stream) {
+  w8a8_status st = check_gemm(xq, sx, wq, sw, M, N, K, 64, K / 2, y_bf16);
+  if (st != W8A8_OK || M == 0 || N == 0) return st;
+  if (!gx || !gw) return W8A8_ERR_NULL;
+  if (!aligned4(gx) || !aligned4(gw)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_gemm_nvfp4(xq, sx, gx, wq, sw, gw, M, N, K, y_bf16,
+                                            as_stream(stream)));
+}
+
 w8a8_status w8a8_channel_absmax(const void* x_bf16, int64_t R, int64_t K, float* amax,
                                 void* stream) {
   w8a8_status st = check_dims(R, K);

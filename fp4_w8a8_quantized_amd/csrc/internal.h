@@ -51,6 +51,11 @@ hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, c
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                    hipStream_t st);
+hipError_t launch_quantize_nvfp4(const void* x, int64_t R, int64_t K, bool given, void* q,
+                                 uint8_t* sc, float* g, hipStream_t st);
+hipError_t launch_gemm_nvfp4(const void* xq, const uint8_t* xs, const float* gx, const void* wq,
+                             const uint8_t* ws, const float* gw, int64_t M, int64_t N, int64_t K,
+                             void* y, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
                              const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t st);

@@ -1,0 +1,285 @@
+// NVFP4 on gfx950: two-level quantization (an fp32 scale per tensor, an E4M3 scale per
+// 16 elements, E2M1 elements) and the W4A4 GEMM over it. The format and its steps are the
+// `nvfp4` emulation of "FP8 and FP4 inference, SmoothQuant and activation quantization"
+// (Implementation sketch) and the NVFP4 column of "Low-bit LLM Weights and Activations"
+// §2.4:
+//   g = amax / 2688 (1 for an all-zero tensor);  code_b = e4m3((amax_b / 6) / g);
+//   s_b = dec(code_b) * g, or 1 where that is 0;  q = e2m1(x / s_b).
+//
+// The GEMM. gfx950's block-scaled MFMA takes power-of-two (E8M0) scales on 32-element
+// blocks, so it cannot apply NVFP4's E4M3 scales on 16-element blocks. The product of an
+// E2M1 element and an E4M3 scale has at most 6 significant bits and lies in
+// [2^-10, 2688], so it is exact in fp16: the kernel dequantizes each operand once per
+// workgroup into fp16 (element times dec(code_b)) and contracts with the fp16 MFMA
+// (16x16x32, FP32 accumulate); g_x g_w is applied in the epilogue.
+#include "common.h"
+#include "internal.h"
+
+namespace w8a8 {
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kNvTensorDiv = 2688.0f;   // 448 * 6: largest E4M3 times largest E2M1
+
+__device__ __forceinline__ float nv_tensor_scale(float amax) {
+  return amax == 0.f ? 1.f : amax / kNvTensorDiv;          // IEEE fp32 division
+}
+
+// ------------------------------------------------------------------------- quantization
+// The tensor amax is accumulated, as fp32 bits (non-negative floats order like their
+// bits), in the caller's g slot; the last launch turns it into g.
+__global__ void nv_amax_init(uint32_t* slot) { *slot = 0u; }
+
+__global__ __launch_bounds__(256) void nv_amax_kernel(const u32x4* __restrict__ x, int64_t nchunk,
+                                                      uint32_t* slot) {
+  float m = 0.f;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunk; c += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, chunk_absmax(__builtin_nontemporal_load(x + c)));
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t u = __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (u > __atomic_load_n(slot, __ATOMIC_RELAXED)) atomicMax(slot, u);
+  }
+}
+
+__global__ void nv_amax_to_scale(uint32_t* slot) {
+  *reinterpret_cast<float*>(slot) = nv_tensor_scale(__uint_as_float(*slot));
+}
+
+// One thread per 16-element block: 32 bytes of bf16 in, 8 bytes of codes and one scale
+// byte out. GIVEN: gp holds g; otherwise it holds the tensor amax's bits.
+template <bool GIVEN>
+__global__ __launch_bounds__(256) void nv_quant_kernel(const u32x4* __restrict__ x, int64_t nblk,
+                                                       const uint32_t* __restrict__ gp,
+                                                       u32x2* __restrict__ q, uint8_t* __restrict__ sc) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblk) return;
+  const float g = GIVEN ? __uint_as_float(*gp) : nv_tensor_scale(__uint_as_float(*gp));
+  const u32x4 v0 = __builtin_nontemporal_load(x + 2 * b);
+  const u32x4 v1 = __builtin_nontemporal_load(x + 2 * b + 1);
+  const float amax = fmaxf(chunk_absmax(v0), chunk_absmax(v1));
+  const float t = (amax / 6.0f) / g;                       // two IEEE divisions, in order
+  const uint32_t code = pack_e4m3x4(clamp448(t), 0.f, 0.f, 0.f) & 0xFFu;
+  float s = __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * g;
+  if (s == 0.f) s = 1.f;
+  const float rcp = 1.0f / s;
+  const bool shortcut = s >= 0x1p-60f && s <= 0x1p60f;     // div_static is exact there
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float lo = bf16_lo(w[i]), hi = bf16_hi(w[i]);
+    const uint32_t cl = e2m1_code(shortcut ? div_static(lo, s, rcp) : lo / s);
+    const uint32_t ch = e2m1_code(shortcut ? div_static(hi, s, rcp) : hi / s);
+    out[i >> 2] |= (cl | (ch << 4)) << (8 * (i & 3));
+  }
+  q[b] = u32x2{out[0], out[1]};
+  sc[b] = (uint8_t)code;
+}
+
+// --------------------------------------------------------------------------------- GEMM
+constexpr int kNvBM = 256, kNvBN = 128, kNvBK = 64;      // K step: 64 elements
+constexpr int kNvThreads = 256;
+constexpr int kNvRow = kNvBK * 2;                         // fp16 row of a stage: 128 bytes
+constexpr int kNvXT = kNvBM * kNvRow, kNvWT = kNvBN * kNvRow, kNvStage = kNvXT + kNvWT;
+
+// 16-byte chunk c of fp16 row r sits at slot c ^ ((r >> 1) & 7): the MFMA fragment reads
+// (16 rows x chunks g or g + 4) and the dequantizer's row writes are free of bank conflicts.
+__device__ __forceinline__ int nv_off(int row, int chunk) {
+  return row * kNvRow + ((chunk ^ ((row >> 1) & 7)) << 4);
+}
+
+// fp16 multiplier of a block relative to g: dec(code) exactly. A zero code means s_b = 1,
+// i.e. 1 / g. Such a block has amax_b <= 6 g 2^-10 while a nonzero element needs
+// |x| > 0.25, so its elements are all zero unless g > 2^10 / 24 (about 42.7); below that
+// the multiplier is irrelevant and 0 is used.
+__device__ __forceinline__ _Float16 nv_block_mul(uint32_t code, float inv_g_zero) {
+  return code ? (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)code, 0) : (_Float16)inv_g_zero;
+}
+
+// 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) times the block
+// multiplier, as 8 fp16 (one 16-byte chunk of a stage row).
+__device__ __forceinline__ u32x4 nv_dequant8(uint32_t w, _Float16 mul) {
+  const f16x2 m2 = {mul, mul};
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * m2;
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * m2;
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * m2;
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * m2;
+  return u32x4{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+               __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+}
+
+// A 256 x 128 tile per workgroup of 4 waves (wave tile 128 x 64: 8 x 4 subtiles of 16x16).
+// Per K step every thread fetches its share of the next step's codes and scales (X row t,
+// 64 elements; W row t / 2, half t % 2), computes on the current fp16 stage, then
+// dequantizes its share into the other stage; one barrier per step.
+__global__ void __launch_bounds__(256)
+gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                  const float* __restrict__ gx, const uint8_t* __restrict__ wq,
+                  const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,
+                  uint16_t* __restrict__ y, int tiles_m, int vec_store) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kNvStage];
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  int b = blockIdx.x;
+  const int nb = gridDim.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // tiles sharing W on one XCD
+  const int tm = b % tiles_m, tn = b / tiles_m;
+  const int m0 = tm * kNvBM, n0 = tn * kNvBN;
+  const int ksteps = K / kNvBK;
+  const int64_t kb = K / 2, ks16 = K / 16;                 // bytes per row: codes, scales
+
+  const float g_x = *gx, g_w = *gw;
+  const float zx = g_x > 42.f ? 1.f / g_x : 0.f, zw = g_w > 42.f ? 1.f / g_w : 0.f;
+
+  // this thread's rows (past M or N: the last row again; never stored)
+  const int xr = min(m0 + t, M - 1);
+  const int wr = min(n0 + (t >> 1), N - 1), wh = t & 1;
+  const uint8_t* xrow = xq + (int64_t)xr * kb;
+  const uint8_t* xsrow = xs + (int64_t)xr * ks16;
+  const uint8_t* wrow = wq + (int64_t)wr * kb + 16 * wh;
+  const uint8_t* wsrow = ws + (int64_t)wr * ks16 + 2 * wh;
+
+  u32x4 xa, xb, wa;
+  uint32_t xsc, wsc;
+  auto fetch = [&](int k) {
+    xa = *reinterpret_cast<const u32x4*>(xrow + 32 * k);
+    xb = *reinterpret_cast<const u32x4*>(xrow + 32 * k + 16);
+    xsc = *reinterpret_cast<const uint32_t*>(xsrow + 4 * k);
+    wa = *reinterpret_cast<const u32x4*>(wrow + 32 * k);
+    wsc = *reinterpret_cast<const uint16_t*>(wsrow + 4 * k);
+  };
+  auto store = [&](int stage) {
+    uint8_t* X = lds + stage * kNvStage;
+    uint8_t* W = X + kNvXT;
+    const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {                          // chunk c: elements 8c .. 8c+7
+      const _Float16 mul = nv_block_mul((xsc >> (8 * (c >> 1))) & 0xFFu, zx);
+      *reinterpret_cast<u32x4*>(X + nv_off(t, c)) = nv_dequant8(xw[c], mul);
+    }
+    const uint32_t ww[4] = {wa.x, wa.y, wa.z, wa.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const _Float16 mul = nv_block_mul((wsc >> (8 * (c >> 1))) & 0xFFu, zw);
+      *reinterpret_cast<u32x4*>(W + nv_off(t >> 1, 4 * wh + c)) = nv_dequant8(ww[c], mul);
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, g = lane >> 4;
+  const int xrow0 = wm * 128, wrow0 = wn * 64;
+
+  fetch(0);
+  store(0);
+  __syncthreads();
+  for (int k = 0; k < ksteps; ++k) {
+    if (k + 1 < ksteps) fetch(k + 1);
+    const uint8_t* X = lds + (k & 1) * kNvStage;
+    const uint8_t* W = X + kNvXT;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {                          // two K32 MFMA steps
+      f16x8 xf[8], wf[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        xf[i] = *reinterpret_cast<const f16x8*>(X + nv_off(xrow0 + 16 * i + fr, 4 * s + g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wf[j] = *reinterpret_cast<const f16x8*>(W + nv_off(wrow0 + 16 * j + fr, 4 * s + g));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xf[i], acc[j][i], 0, 0, 0);
+    }
+    if (k + 1 < ksteps) store((k + 1) & 1);
+    __syncthreads();
+  }
+
+  // Epilogue: y = bf16(acc * g_x g_w), staged through LDS as whole rows.
+  constexpr int RS = kNvBN * 2 + 16;
+  static_assert(kNvBM * RS <= 2 * kNvStage, "output tile must fit in the stage LDS");
+  const float gxw = g_x * g_w;
+  // lane l holds output row 16 i + (l & 15) and columns 16 j + 4 (l >> 4) + r
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rl = xrow0 + 16 * i + fr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cl = wrow0 + 16 * j + 4 * g;
+      const u32x2 o = {pack_bf16x2(acc[j][i][0] * gxw, acc[j][i][1] * gxw),
+                       pack_bf16x2(acc[j][i][2] * gxw, acc[j][i][3] * gxw)};
+      *reinterpret_cast<u32x2*>(lds + rl * RS + cl * 2) = o;
+    }
+  }
+  __syncthreads();
+  constexpr int CPR = kNvBN / 8;                           // 16-byte chunks per output row
+  for (int c = t; c < kNvBM * CPR; c += kNvThreads) {
+    const int rl = c / CPR, ch = c - rl * CPR;
+    const int m = m0 + rl, n = n0 + ch * 8;
+    if (m >= M || n >= N) continue;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + rl * RS + ch * 16);
+    uint16_t* yr = y + (size_t)m * N + n;
+    if (vec_store && n + 7 < N) {
+      *reinterpret_cast<u32x4*>(yr) = v;
+    } else {
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (n + e >= N) break;
+        yr[e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_nvfp4(const void* x, int64_t R, int64_t K, bool given, void* q,
+                                 uint8_t* sc, float* g, hipStream_t st) {
+  const int64_t nblk = R * K / 16;
+  uint32_t* slot = reinterpret_cast<uint32_t*>(g);
+  if (!given) {
+    const int64_t nchunk = R * K / 8;
+    const int64_t want = (nchunk + 255) / 256;
+    const unsigned blocks = (unsigned)(want < 2048 ? want : 2048);
+    hipLaunchKernelGGL(nv_amax_init, dim3(1), dim3(1), 0, st, slot);
+    hipLaunchKernelGGL(nv_amax_kernel, dim3(blocks), dim3(256), 0, st,
+                       reinterpret_cast<const u32x4*>(x), nchunk, slot);
+  }
+  const dim3 grid((unsigned)((nblk + 255) / 256));
+  if (given)
+    hipLaunchKernelGGL(nv_quant_kernel<true>, grid, dim3(256), 0, st,
+                       reinterpret_cast<const u32x4*>(x), nblk, (const uint32_t*)slot,
+                       reinterpret_cast<u32x2*>(q), sc);
+  else
+    hipLaunchKernelGGL(nv_quant_kernel<false>, grid, dim3(256), 0, st,
+                       reinterpret_cast<const u32x4*>(x), nblk, (const uint32_t*)slot,
+                       reinterpret_cast<u32x2*>(q), sc);
+  if (!given) hipLaunchKernelGGL(nv_amax_to_scale, dim3(1), dim3(1), 0, st, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4(const void* xq, const uint8_t* xs, const float* gx, const void* wq,
+                             const uint8_t* ws, const float* gw, int64_t M, int64_t N, int64_t K,
+                             void* y, hipStream_t st) {
+  const int tiles_m = (int)((M + kNvBM - 1) / kNvBM);
+  const int tiles_n = (int)((N + kNvBN - 1) / kNvBN);
+  hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kNvThreads), 0, st,
+                     (const uint8_t*)xq, xs, gx, (const uint8_t*)wq, ws, gw, (int)M, (int)N, (int)K,
+                     (uint16_t*)y, tiles_m, (int)((N % 8) == 0));
+  return hipGetLastError();
+}
+
+}  // namespace w8a8

@@ -227,20 +227,6 @@ hipError_t launch_quantize_block(const void* w, int64_t N, int64_t K, void* q, f
 // 32-element block. Scale exponent e = floor(log2 amax) - 2 (E2M1's top binade is 2^2),
 // clamped to [-127, 127], 0 for an all-zero block; elements x * 2^-e (exact) are
 // rounded to E2M1 half-to-even and saturated to +-6.
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 28) & 8u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t c;
-  if (a < 0x3F800000u) {                 // |v| < 1: grid step 0.5 -> rint(2|v|) in 0..2
-    c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-  } else {                               // keep one mantissa bit, half-to-even
-    const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
-    c = min((r >> 22) - 252u, 7u);
-  }
-  return sign | c;
-}
-
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x,
                                                           int64_t nchunk, uint8_t* __restrict__ q,
                                                           uint8_t* __restrict__ sc) {

@@ -1,5 +1,5 @@
 /*
- * w8a8.h - C ABI of the MI355X (gfx950) W8A8 / block-scaled FP8 / INT8 / MXFP4 library.
+ * w8a8.h - C ABI of the MI355X (gfx950) W8A8 / block-scaled FP8 / INT8 / MXFP4 / NVFP4 library.
  *
  * The calls follow the problem statement of three pages:
  *   [P-FP8FP4]  "FP8 and FP4 inference, SmoothQuant and activation quantization"
@@ -202,6 +202,43 @@ w8a8_status w8a8_quantize_mxfp4(const void* x_bf16, int64_t R, int64_t K, void* 
  * K % 256 == 0. */
 w8a8_status w8a8_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
                             const uint8_t* sw, int64_t M, int64_t N, int64_t K,
+                            void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * NVFP4 ([P-FP8FP4] "Implementation sketch", the `nvfp4` emulation, and the measured-model
+ * section; [P-LOWBIT] §2.4: E2M1 elements, one E4M3 scale per 16 elements, 4.5 bits per
+ * element, plus one fp32 scale per tensor).
+ *
+ * Quantize the rows of a bf16 [R, K] matrix (activations or weights):
+ *   g = amax(|x| over the whole matrix) / 2688 (2688 = 448 * 6; g = 1 for an all-zero
+ *       matrix), or the caller's g;
+ *   per 16-element block b along K: code_b = E4M3FN((amax_b / 6) / g) (IEEE fp32 divisions
+ *       in that order, round to nearest even, saturating at 448);
+ *   s_b = dec(code_b) * g in fp32, replaced by 1 where it is 0;
+ *   element code = E2M1(x / s_b) (IEEE fp32 quotient, nearest even, saturating at +-6).
+ *   q_packed: [R, K/2] bytes (element 2i in the low nibble)   scale_e4m3: [R, K/16] bytes
+ *   g: one fp32 on the device (4-byte aligned).               K % 16 == 0.
+ * scale_mode W8A8_NVFP4_SCALE_COMPUTE computes g from x and writes it to *g (the slot holds
+ * the running amax while the call's kernels run); W8A8_NVFP4_SCALE_GIVEN reads *g, which
+ * must be finite and positive (it is not checked: it lives on the device). R == 0 or
+ * K == 0 writes nothing. Any other scale_mode is W8A8_ERR_UNSUPPORTED.
+ */
+typedef enum { W8A8_NVFP4_SCALE_COMPUTE = 0, W8A8_NVFP4_SCALE_GIVEN = 1 } w8a8_nvfp4_scale_mode;
+w8a8_status w8a8_quantize_nvfp4(const void* x_bf16, int64_t R, int64_t K, int scale_mode,
+                                void* q_packed, uint8_t* scale_e4m3, float* g, void* stream);
+
+/* NVFP4 x NVFP4 GEMM:
+ *   y[m,n] = bf16_rne( sum_b s_x[m,b] s_w[n,b] sum_{k in b} dec(xq[m,k]) dec(wq[n,k]) )
+ * with s as above (from the scale codes and gx / gw, each one fp32 on the device),
+ * accumulated in FP32. The operands are dequantized to fp16 (element times dec(code_b),
+ * exact) and contracted on the fp16 matrix cores; gx gw is applied after the reduction.
+ * Two cases differ from the definition by fp32 rounding only: a block whose scale code is
+ * 0 uses 1/g rounded to fp16, and a g small enough (below about 2^-117) that dec * g is
+ * an fp32 subnormal.
+ *   xq [M, K/2], wq [N, K/2] packed; sx [M, K/16], sw [N, K/16] E4M3 codes.  K % 64 == 0.
+ */
+w8a8_status w8a8_gemm_nvfp4(const void* xq, const uint8_t* sx, const float* gx, const void* wq,
+                            const uint8_t* sw, const float* gw, int64_t M, int64_t N, int64_t K,
                             void* y_bf16, void* stream);
 
 /* ------------------------------------------------------------------------------------

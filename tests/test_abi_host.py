@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     for n in ["w8a8_quantize_per_token", "w8a8_quantize_weight_per_channel", "w8a8_gemm", "w8a8_gemm_ex",
               "w8a8_quantize_per_token_group", "w8a8_quantize_weight_block", "w8a8_gemm_blockscaled",
               "w8a8_quantize_mxfp4", "w8a8_gemm_mxfp4", "w8a8_channel_absmax",
-              "w8a8_smoothquant_scales", "w8a8_smooth_apply", "w8a8_status_string"]:
+              "w8a8_smoothquant_scales", "w8a8_smooth_apply", "w8a8_status_string",
+              "w8a8_quantize_nvfp4", "w8a8_gemm_nvfp4"]:
         assert n in names
 
 
@@ -140,6 +141,24 @@ def test_mxfp4_validation(L):
     assert L.w8a8_gemm_mxfp4(A, A, A, A, 4, 4, 128, A, None) == EUNSUP   # K % 256
     assert L.w8a8_gemm_mxfp4(A, A, A, A, 4, 4, 256, None, None) == ENULL
     assert L.w8a8_gemm_mxfp4(A, MIS, A, A, 4, 4, 256, A, None) == EALIGN
+
+
+def test_nvfp4_validation(L):
+    qn = L.w8a8_quantize_nvfp4
+    assert qn(A, 4, 40, 0, A, A, A, None) == EUNSUP          # K % 16
+    assert qn(A, 4, 64, 2, A, A, A, None) == EUNSUP          # scale mode
+    assert qn(A, 4, 64, 0, A, A, None, None) == ENULL        # g
+    assert qn(A, 4, 64, 1, A, None, A, None) == ENULL
+    assert qn(A, 4, 64, 0, A, A, 0x10002, None) == EALIGN    # g 4-byte aligned
+    assert qn(A, 4, 64, 0, MIS, A, A, None) == EALIGN
+    assert qn(A, -1, 64, 0, A, A, A, None) == ESHAPE
+    assert qn(None, 0, 64, 0, None, None, None, None) == OK  # empty: nothing written
+    gn = L.w8a8_gemm_nvfp4
+    assert gn(A, A, A, A, A, A, 4, 4, 96, A, None) == EUNSUP   # K % 64
+    assert gn(A, A, None, A, A, A, 4, 4, 64, A, None) == ENULL
+    assert gn(A, A, A, A, A, 0x10002, 4, 4, 64, A, None) == EALIGN
+    assert gn(A, MIS, A, A, A, A, 4, 4, 64, A, None) == EALIGN
+    assert gn(A, A, A, A, A, A, 0, 4, 64, A, None) == OK
 
 
 def test_smoothquant_validation(L):

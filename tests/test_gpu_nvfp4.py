@@ -1,0 +1,122 @@
+"""GPU parity: NVFP4 quantization (codes, E4M3 block scales and the tensor scale, bit for
+bit) and the NVFP4 GEMM (within |y - y_ref| <= 1e-2 (|y_ref| + rms(y_ref))) against the
+oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+import fp4_w8a8_quantized_amd as w8
+from oracle import gemm as G
+from oracle import nvfp4 as N
+from tests.gpu_util import bf16_to_f64, bits_u8, f32, first_mismatch, need_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _bf16(v):
+    return synthetic.to_bf16_bits(np.asarray(v, np.float64))
+
+
+def _x(M, K, seed, spread=4.0):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((M, K)) * np.exp2(rng.uniform(-spread, spread, (M, 1)))
+    if K >= 64:
+        v[:, rng.choice(K, max(1, K // 1000), replace=False)] *= 100.0
+    return _bf16(v)
+
+
+def _check_quant(xb, q, s, g, g_given=None, what=""):
+    oq, os_, og = N.quantize_nvfp4(xb, g=g_given)
+    assert np.float32(f32(g)[0]) == og, f"{what}: g {f32(g)[0]!r} vs {og!r}"
+    assert np.array_equal(bits_u8(s), os_), f"{what}: scales {first_mismatch(bits_u8(s), os_)}"
+    assert np.array_equal(bits_u8(q), oq), f"{what}: codes {first_mismatch(bits_u8(q), oq)}"
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (3, 48), (300, 4096), (2048, 4096), (129, 14336)])
+def test_quantize_nvfp4(M, K):
+    need_gpu()
+    xb = _x(M, K, M * 7 + K)
+    q, s, g = w8.quantize_nvfp4(to_dev_bf16(xb))
+    torch.cuda.synchronize()
+    _check_quant(xb, q, s, g, what=f"{M}x{K}")
+
+
+@pytest.mark.parametrize("factor", [0.25, 1.0, 8.0, 2.0 ** -40, 2.0 ** 40])
+def test_quantize_nvfp4_given_scale(factor):
+    """A caller's g: below the natural one (saturating blocks and elements), equal, above,
+    and far outside (scale codes 0 or all saturated)."""
+    need_gpu()
+    xb = _x(64, 512, 9)
+    g0 = N.tensor_scale(xb)
+    gg = np.float32(g0 * np.float32(factor))
+    g = torch.tensor([float(gg)], dtype=torch.float32, device="cuda")
+    q, s, g_out = w8.quantize_nvfp4(to_dev_bf16(xb), g=g)
+    torch.cuda.synchronize()
+    assert g_out.data_ptr() == g.data_ptr()
+    _check_quant(xb, q, s, g, g_given=gg, what=f"g x {factor}")
+
+
+def test_quantize_nvfp4_special_tensors():
+    need_gpu()
+    cases = {
+        "zeros": np.zeros((2, 32)),
+        "zero-scale block": np.concatenate([[2.0 ** 20], np.ones(31)])[None, :],
+        "signed zeros and ties": np.array([[-0.0, 0.0, 0.25, -0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0,
+                                            -5.0, 6.0, 7.0, -100.0, 1e-3, -1e-30] * 2]),
+        "huge and tiny": np.array([[3.0e38, -1e-38, 1.0, 2.0 ** -100] * 8]),
+        "tiny tensor": np.array([[1e-38, -2e-38, 3e-39, 0.0] * 8]),
+    }
+    for what, v in cases.items():
+        xb = _bf16(v)
+        q, s, g = w8.quantize_nvfp4(to_dev_bf16(xb))
+        torch.cuda.synchronize()
+        _check_quant(xb, q, s, g, what=what)
+
+
+def _gemm_compare(xb, wb, what, rows=None):
+    x, w = to_dev_bf16(xb), to_dev_bf16(wb)
+    xq, sx, gx = w8.quantize_nvfp4(x)
+    wq, sw, gw = w8.quantize_nvfp4(w)
+    y = w8.gemm_nvfp4(xq, sx, gx, wq, sw, gw)
+    torch.cuda.synchronize()
+    rows = np.arange(xb.shape[0]) if rows is None else rows
+    ogx = N.tensor_scale(xb)
+    oxq, osx, _ = N.quantize_nvfp4(xb[rows], g=ogx)
+    owq, osw, ogw = N.quantize_nvfp4(wb)
+    assert np.array_equal(bits_u8(xq)[rows], oxq) and np.array_equal(bits_u8(sx)[rows], osx)
+    assert np.array_equal(bits_u8(wq), owq) and np.array_equal(bits_u8(sw), osw)
+    assert f32(gx)[0] == ogx and f32(gw)[0] == ogw
+    ok, worst = G.within_tolerance(bf16_to_f64(y)[rows], N.gemm_nvfp4_ref(oxq, osx, ogx, owq, osw, ogw), TOL)
+    assert ok, f"{what}: worst error / bound = {worst:.3f}"
+
+
+@pytest.mark.parametrize("M,N_,K", [(1, 1, 64), (17, 130, 128), (300, 549, 256), (257, 129, 640),
+                                    (64, 256, 4096), (513, 1000, 1024)])
+def test_gemm_nvfp4_ragged(M, N_, K):
+    need_gpu()
+    xb = _x(M, K, M * 31 + N_ * 7 + K)
+    wb = _bf16(np.random.default_rng(M + N_ + K).standard_normal((N_, K)) * 0.02)
+    _gemm_compare(xb, wb, f"{M}x{N_}x{K}")
+
+
+def test_gemm_nvfp4_zero_scale_blocks():
+    """g > 42: blocks whose scale code is 0 carry nonzero elements at s = 1."""
+    need_gpu()
+    rng = np.random.default_rng(77)
+    v = rng.standard_normal((40, 256))
+    v[:, 0] = 2.0 ** 20                     # tensor amax 2^20: g = 390, small blocks code 0
+    wv = rng.standard_normal((70, 256))
+    _gemm_compare(_bf16(v), _bf16(wv), "zero-scale blocks")
+
+
+def test_gemm_nvfp4_full_size_sampled():
+    """The 8192 x 8192 x 8192 MXFP4 workload's inputs, quantized to NVFP4."""
+    need_gpu()
+    xb, wb = synthetic.mxfp4()
+    rng = np.random.default_rng(45)
+    rows = np.sort(np.concatenate([[0, xb.shape[0] - 1], rng.choice(xb.shape[0], 30, replace=False)]))
+    _gemm_compare(xb, wb, "nvfp4 8192^3", rows=rows)
