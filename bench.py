@@ -18,6 +18,8 @@ Other workloads (`--workload decode|blockscaled|mxfp4|all`) print one JSON line 
   blockscaled  M = 4096, K = 7168, N = 18432 with 1x128 activation groups and 128x128
                weight blocks (group quantize + block-scaled GEMM timed).
   mxfp4        M = N = K = 8192, MXFP4 operands (MX quantize of X + FP4 GEMM timed).
+  nvfp4        the same 8192^3 inputs as NVFP4 (tensor-scale pass + quantize of X, and the
+               GEMM on the fp16 matrix cores, timed).
   epilogue     the prefill linears with the full epilogue: + bf16 bias, SiLU, and FP8
                output requantized with a static scale (calibrated once, untimed), against
                the plain bf16 epilogue on the same inputs.
@@ -43,6 +45,7 @@ if ROOT not in sys.path:
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA (INT8: 5000 TOPS)
 FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 MFMA
 HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
+FP16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16 / bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_gemm_prefill_8b_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "fp4_w8a8_quantized_amd", "csrc", f)
                 for f in ("gemm_pp.hip", "common.h")]
@@ -54,7 +57,7 @@ def _parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "blockscaled", "mxfp4", "epilogue", "static", "all"])
+                   choices=["prefill", "decode", "blockscaled", "mxfp4", "nvfp4", "epilogue", "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=256,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
@@ -641,6 +644,56 @@ def run_mxfp4(args, c: Ctx):
     return rec
 
 
+# ----------------------------------------------------------------------------- NVFP4
+def run_nvfp4(args, c: Ctx):
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh = c.torch, c.w8, c.L, c.sh
+    M, K, N = synthetic.MXFP4_SHAPE
+    xb, wb = synthetic.mxfp4()
+    x = c.bf16(xb)
+    w = c.bf16(wb)
+    wq, sw, gw = w8.quantize_nvfp4(w)
+    del w
+    xq = torch.empty((M, K // 2), dtype=torch.uint8, device=c.dev)
+    sx = torch.empty((M, K // 16), dtype=torch.uint8, device=c.dev)
+    gx = torch.empty((1,), dtype=torch.float32, device=c.dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+    torch.cuda.synchronize()
+    wall, q_s, g_s = _timed_pair(
+        args, c,
+        lambda: c.check(L.w8a8_quantize_nvfp4(x.data_ptr(), M, K, 0, xq.data_ptr(), sx.data_ptr(),
+                                              gx.data_ptr(), sh)),
+        lambda: c.check(L.w8a8_gemm_nvfp4(xq.data_ptr(), sx.data_ptr(), gx.data_ptr(), wq.data_ptr(),
+                                          sw.data_ptr(), gw.data_ptr(), M, N, K, y.data_ptr(), sh)))
+    flops = 2.0 * M * N * K
+    achieved = flops / g_s / 1e12
+    rec = _base_record(args, "NVFP4 GEMM TFLOP/s (tensor-scale + NVFP4 quantize + GEMM), % of fp16 MFMA peak",
+                       flops / wall / 1e12, "TFLOP/s", wall * 1e3, "fp4_e2m1+e4m3 (fp16 MFMA)",
+                       {"workload": "NVFP4 operands (E2M1, E4M3 scale per 16 along K, fp32 tensor scale), "
+                                    "dequantized to fp16 per workgroup", "M": M, "K": K, "N": N})
+    rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(achieved / FP16_PEAK_TFLOPS, 4), "traffic": None}
+    q_bytes = 4.5 * M * K + M * K / 16
+    rec["kernels"] = {"gemm_us": round(g_s * 1e6, 1), "nv_quant_us": round(q_s * 1e6, 1),
+                      "nv_quant_GBps": round(q_bytes / q_s / 1e9, 1)}
+    if not args.no_cpu_baseline:
+        from oracle import nvfp4 as NV
+        rows, cols = 64, 2048
+        gxo = NV.tensor_scale(xb)
+        owq, osw, ogw = NV.quantize_nvfp4(wb[:cols])
+        t0 = time.perf_counter()
+        oxq, osx, _ = NV.quantize_nvfp4(xb[:rows], g=gxo)
+        np.asarray(NV.gemm_nvfp4_ref(oxq, osx, gxo, owq, osw, ogw)).sum()
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": round(2.0 * rows * cols * K / dt / 1e12, 6), "unit": "TFLOP/s",
+                               "cores": _threads(), "kind": "oracle",
+                               "sample": f"{rows} tokens x {cols} outputs x K={K} (NVFP4 quantize with the "
+                                         f"full tensor's scale + fp64 contraction), weights pre-quantized; "
+                                         f"{dt:.1f} s"}
+    return rec
+
+
 def main():
     args = _parse_args()
     if args.gpus != 1:
@@ -668,7 +721,7 @@ def main():
     c = Ctx()
     runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
             "epilogue": run_epilogue, "static": run_static,
-            "mxfp4": run_mxfp4}
+            "mxfp4": run_mxfp4, "nvfp4": run_nvfp4}
     names = list(runs) if args.workload == "all" else [args.workload]
     for name in names:
         rec = runs[name](args, c)

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void nv_quant_kernel(const u32x4* __restrict__
 
 // --------------------------------------------------------------------------------- GEMM
 constexpr int kNvBM = 256, kNvBN = 128, kNvBK = 64;      // K step: 64 elements
-constexpr int kNvThreads = 256;
+constexpr int kNvThreads = 512;
 constexpr int kNvRow = kNvBK * 2;                         // fp16 row of a stage: 128 bytes
 constexpr int kNvXT = kNvBM * kNvRow, kNvWT = kNvBN * kNvRow, kNvStage = kNvXT + kNvWT;
 
@@ -99,7 +99,8 @@ __device__ __forceinline__ int nv_off(int row, int chunk) {
 // |x| > 0.25, so its elements are all zero unless g > 2^10 / 24 (about 42.7); below that
 // the multiplier is irrelevant and 0 is used.
 __device__ __forceinline__ _Float16 nv_block_mul(uint32_t code, float inv_g_zero) {
-  return code ? (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)code, 0) : (_Float16)inv_g_zero;
+  const float d = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);   // decoded unconditionally:
+  return (_Float16)(code == 0u ? inv_g_zero : d);               // a select, not a branch
 }
 
 // 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) times the block
@@ -114,11 +115,13 @@ __device__ __forceinline__ u32x4 nv_dequant8(uint32_t w, _Float16 mul) {
                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
 }
 
-// A 256 x 128 tile per workgroup of 4 waves (wave tile 128 x 64: 8 x 4 subtiles of 16x16).
-// Per K step every thread fetches its share of the next step's codes and scales (X row t,
-// 64 elements; W row t / 2, half t % 2), computes on the current fp16 stage, then
-// dequantizes its share into the other stage; one barrier per step.
-__global__ void __launch_bounds__(256)
+// A 256 x 128 tile per workgroup of 8 waves (two per SIMD), wave tile 64 x 64 (4 x 4
+// subtiles of 16x16), K step 64. Every thread owns a share of each step's codes and scales
+// (X row t/2, half t%2: 32 elements, two blocks; W row t/4, quarter t%4: 16 elements, one
+// block). Step k: fragments and MFMAs for the first K32 half of stage k%2; dequantization
+// of step k+1's share into the other stage, then the fetch of step k+2's share into the
+// freed registers; the second K32 half; one barrier.
+__global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                   const float* __restrict__ gx, const uint8_t* __restrict__ wq,
                   const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,
@@ -126,7 +129,7 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kNvStage];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;
   int b = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // tiles sharing W on one XCD
@@ -139,71 +142,72 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   const float zx = g_x > 42.f ? 1.f / g_x : 0.f, zw = g_w > 42.f ? 1.f / g_w : 0.f;
 
   // this thread's rows (past M or N: the last row again; never stored)
-  const int xr = min(m0 + t, M - 1);
-  const int wr = min(n0 + (t >> 1), N - 1), wh = t & 1;
-  const uint8_t* xrow = xq + (int64_t)xr * kb;
-  const uint8_t* xsrow = xs + (int64_t)xr * ks16;
-  const uint8_t* wrow = wq + (int64_t)wr * kb + 16 * wh;
-  const uint8_t* wsrow = ws + (int64_t)wr * ks16 + 2 * wh;
+  const int xr_l = t >> 1, xh = t & 1, wr_l = t >> 2, wq4 = t & 3;
+  const int xr = min(m0 + xr_l, M - 1), wr = min(n0 + wr_l, N - 1);
+  const uint8_t* xrow = xq + (int64_t)xr * kb + 16 * xh;
+  const uint8_t* xsrow = xs + (int64_t)xr * ks16 + 2 * xh;
+  const uint8_t* wrow = wq + (int64_t)wr * kb + 8 * wq4;
+  const uint8_t* wsrow = ws + (int64_t)wr * ks16 + wq4;
 
-  u32x4 xa, xb, wa;
+  u32x4 xa;
+  u32x2 wa;
   uint32_t xsc, wsc;
   auto fetch = [&](int k) {
     xa = *reinterpret_cast<const u32x4*>(xrow + 32 * k);
-    xb = *reinterpret_cast<const u32x4*>(xrow + 32 * k + 16);
-    xsc = *reinterpret_cast<const uint32_t*>(xsrow + 4 * k);
-    wa = *reinterpret_cast<const u32x4*>(wrow + 32 * k);
-    wsc = *reinterpret_cast<const uint16_t*>(wsrow + 4 * k);
+    xsc = *reinterpret_cast<const uint16_t*>(xsrow + 4 * k);
+    wa = *reinterpret_cast<const u32x2*>(wrow + 32 * k);
+    wsc = wsrow[4 * k];
   };
   auto store = [&](int stage) {
     uint8_t* X = lds + stage * kNvStage;
     uint8_t* W = X + kNvXT;
-    const uint32_t xw[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+    const _Float16 x0 = nv_block_mul(xsc & 0xFFu, zx), x1 = nv_block_mul((xsc >> 8) & 0xFFu, zx);
+    const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {                          // chunk c: elements 8c .. 8c+7
-      const _Float16 mul = nv_block_mul((xsc >> (8 * (c >> 1))) & 0xFFu, zx);
-      *reinterpret_cast<u32x4*>(X + nv_off(t, c)) = nv_dequant8(xw[c], mul);
-    }
-    const uint32_t ww[4] = {wa.x, wa.y, wa.z, wa.w};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const _Float16 mul = nv_block_mul((wsc >> (8 * (c >> 1))) & 0xFFu, zw);
-      *reinterpret_cast<u32x4*>(W + nv_off(t >> 1, 4 * wh + c)) = nv_dequant8(ww[c], mul);
-    }
+    for (int c = 0; c < 4; ++c)                            // chunk 4 xh + c: 8 elements
+      *reinterpret_cast<u32x4*>(X + nv_off(xr_l, 4 * xh + c)) = nv_dequant8(xw[c], c < 2 ? x0 : x1);
+    const _Float16 w0 = nv_block_mul(wsc & 0xFFu, zw);
+    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4)) = nv_dequant8(wa.x, w0);
+    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4 + 1)) = nv_dequant8(wa.y, w0);
   };
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, g = lane >> 4;
-  const int xrow0 = wm * 128, wrow0 = wn * 64;
+  const int xrow0 = wm * 64, wrow0 = wn * 64;
+  // One K32 half of a step: fragments from the stage, then 16 MFMAs.
+  auto half = [&](const uint8_t* X, int s) {
+    const uint8_t* W = X + kNvXT;
+    f16x8 xf[4], wf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      xf[i] = *reinterpret_cast<const f16x8*>(X + nv_off(xrow0 + 16 * i + fr, 4 * s + g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wf[j] = *reinterpret_cast<const f16x8*>(W + nv_off(wrow0 + 16 * j + fr, 4 * s + g));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xf[i], acc[j][i], 0, 0, 0);
+  };
 
   fetch(0);
   store(0);
+  if (ksteps > 1) fetch(1);
   __syncthreads();
   for (int k = 0; k < ksteps; ++k) {
-    if (k + 1 < ksteps) fetch(k + 1);
     const uint8_t* X = lds + (k & 1) * kNvStage;
-    const uint8_t* W = X + kNvXT;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {                          // two K32 MFMA steps
-      f16x8 xf[8], wf[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        xf[i] = *reinterpret_cast<const f16x8*>(X + nv_off(xrow0 + 16 * i + fr, 4 * s + g));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wf[j] = *reinterpret_cast<const f16x8*>(W + nv_off(wrow0 + 16 * j + fr, 4 * s + g));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xf[i], acc[j][i], 0, 0, 0);
+    half(X, 0);
+    if (k + 1 < ksteps) {
+      store((k + 1) & 1);
+      if (k + 2 < ksteps) fetch(k + 2);
     }
-    if (k + 1 < ksteps) store((k + 1) & 1);
+    half(X, 1);
     __syncthreads();
   }
 
@@ -213,7 +217,7 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   const float gxw = g_x * g_w;
   // lane l holds output row 16 i + (l & 15) and columns 16 j + 4 (l >> 4) + r
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     const int rl = xrow0 + 16 * i + fr;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
