@@ -1,4 +1,4 @@
-"""CPU oracle for the W8A8 / block-scaled FP8 / SmoothQuant INT8 / MXFP4 / NVFP4 hot path.
+"""CPU oracle for the W8A8 / block-scaled FP8 / SmoothQuant INT8 / MXFP4 / NVFP4 / W4A16 hot path.
 
 TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or link this
 package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
@@ -31,8 +31,10 @@ Pinning status (what each part is checked against lives in ``tests/test_oracle_*
 * nvfp4.py        pinned (hand-computed grid blocks and scale codes, nearest-value brute
                   force, the zero-scale rule, 4.5 bits per element from [P-LOWBIT] §2.4,
                   triple-loop GEMM)
+* w4a16.py        pinned (metadata sizes printed on [P-LOWBIT] §2.3 / §3.3, a hand-computed
+                  group, nearest-integer brute force, packing, triple-loop GEMM)
 """
 
-from . import formats, quant, gemm, smoothquant, roofline, epilogue, static_scale, nvfp4  # noqa: F401
+from . import formats, quant, gemm, smoothquant, roofline, epilogue, static_scale, nvfp4, w4a16  # noqa: F401
 
-__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue", "static_scale", "nvfp4"]
+__all__ = ["formats", "quant", "gemm", "smoothquant", "roofline", "epilogue", "static_scale", "nvfp4", "w4a16"]
