@@ -53,6 +53,8 @@ _SIGNATURES = {
     "w8a8_gemm_blockscaled": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
     "w8a8_quantize_mxfp4": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm_mxfp4": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
+    "w8a8_quantize_int4": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp],
+    "w8a8_gemm_w4a16": [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
     "w8a8_quantize_nvfp4": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm_nvfp4": [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp],
     "w8a8_channel_absmax": [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp],
@@ -357,6 +359,34 @@ def gemm_nvfp4(xq, sx, gx, wq, sw, gw, out=None) -> torch.Tensor:
     _check(lib().w8a8_gemm_nvfp4(xq.data_ptr(), sx.data_ptr(), gx.data_ptr(), wq.data_ptr(),
                                  sw.data_ptr(), gw.data_ptr(), M, N, K, y.data_ptr(), _stream(xq)),
            "w8a8_gemm_nvfp4")
+    return y
+
+
+# ------------------------------------------------------------------------------ W4A16
+def quantize_int4(w: torch.Tensor):
+    """bf16 [N, K] -> (packed INT4 uint8 [N, K/2], fp16 group scales [N, K/128])."""
+    _dev(w, "w", torch.bfloat16, 2)
+    N, K = w.shape
+    q = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    s = torch.empty((N, K // 128), dtype=torch.float16, device=w.device)
+    _check(lib().w8a8_quantize_int4(w.data_ptr(), N, K, q.data_ptr(), s.data_ptr(), _stream(w)),
+           "w8a8_quantize_int4")
+    return q, s
+
+
+def gemm_w4a16(x: torch.Tensor, q: torch.Tensor, s: torch.Tensor, out=None) -> torch.Tensor:
+    """y bf16 [M, N] = x (bf16 [M, K]) times the INT4 weights (packed [N, K/2], fp16 [N, K/128])."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(q, "q", torch.uint8, 2)
+    _dev(s, "s", torch.float16, 2)
+    M, K = x.shape
+    N = q.shape[0]
+    if q.shape[1] * 2 != K or tuple(s.shape) != (N, K // 128):
+        raise ValueError("W4A16 operand shapes disagree")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _dev(y, "out", torch.bfloat16, 2)
+    _check(lib().w8a8_gemm_w4a16(x.data_ptr(), q.data_ptr(), s.data_ptr(), M, N, K, y.data_ptr(),
+                                 _stream(x)), "w8a8_gemm_w4a16")
     return y
 
 

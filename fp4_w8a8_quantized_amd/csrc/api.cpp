@@ -209,6 +209,31 @@ w8a8_status w8a8_gemm_nvfp4(const void* xq, const uint8_t* sx, const float* gx, 
                                             as_stream(stream)));
 }
 
+w8a8_status w8a8_quantize_int4(const void* w_bf16, int64_t N, int64_t K, void* q_packed,
+                               uint16_t* scale_f16, void* stream) {
+  w8a8_status st = check_dims(N, K);
+  if (st != W8A8_OK) return st;
+  if (K % 128 != 0) return W8A8_ERR_UNSUPPORTED;
+  if (N == 0 || K == 0) return W8A8_OK;
+  if (!w_bf16 || !q_packed || !scale_f16) return W8A8_ERR_NULL;
+  if (!aligned16(w_bf16) || !aligned16(q_packed) || !aligned16(scale_f16)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_quantize_int4(w_bf16, N, K, q_packed, scale_f16, as_stream(stream)));
+}
+
+w8a8_status w8a8_gemm_w4a16(const void* x_bf16, const void* q_packed, const uint16_t* scale_f16,
+                            int64_t M, int64_t N, int64_t K, void* y_bf16, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return W8A8_ERR_SHAPE;
+  if (K == 0 || K % 128 != 0) return W8A8_ERR_UNSUPPORTED;
+  if (M > kMaxOperandBytes / (2 * K) || N > kMaxOperandBytes / K) return W8A8_ERR_SHAPE;
+  if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return W8A8_ERR_SHAPE;
+  if (M == 0 || N == 0) return W8A8_OK;
+  if (!x_bf16 || !q_packed || !scale_f16 || !y_bf16) return W8A8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(q_packed) || !aligned16(scale_f16) || !aligned16(y_bf16))
+    return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_gemm_w4a16(x_bf16, q_packed, scale_f16, M, N, K, y_bf16,
+                                            as_stream(stream)));
+}
+
 w8a8_status w8a8_channel_absmax(const void* x_bf16, int64_t R, int64_t K, float* amax,
                                 void* stream) {
   w8a8_status st = check_dims(R, K);

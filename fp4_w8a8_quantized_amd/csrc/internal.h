@@ -56,6 +56,10 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t R, int64_t K, bool given
 hipError_t launch_gemm_nvfp4(const void* xq, const uint8_t* xs, const float* gx, const void* wq,
                              const uint8_t* ws, const float* gw, int64_t M, int64_t N, int64_t K,
                              void* y, hipStream_t st);
+hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, uint16_t* sc,
+                                hipStream_t st);
+hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
+                             int64_t K, void* y, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
                              const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t st);

@@ -1,0 +1,227 @@
+// W4A16 on gfx950: symmetric INT4 weights with one fp16 scale per group of 128 along K,
+// and the weight-only decode GEMM y = X W^T with bf16 activations ("Low-bit LLM Weights and
+// Activations" §2.3: q in [-7, 7], S = max|x| / 7 per group; §3.3: unpack and dequantize
+// the weights next to a 16-bit matrix product; weight traffic is the only gain, so this is
+// a decode kernel).
+//
+// Quantization: four lanes per group (32 elements each); S = fp16(fp32(amax) / 7) (1 for an
+// all-zero group, 65504 where fp16 overflows); q = clamp(rint(x / S), -7, 7) with the IEEE
+// quotient; codes are 4-bit two's complement, element 2i in the low nibble.
+//
+// GEMM: organised like the few-token FP8 kernel, around streaming W once at HBM rate. A
+// workgroup owns 16 NW weight rows; its WPB waves split the K groups (wave w: groups w,
+// w + WPB, ...). Per group a lane reads 16 bytes of its row (32 codes, K offsets 32 g + 0..31
+// of the group for lane group g = lane >> 4), converts them to bf16 (exact small integers)
+// and feeds four 16x16x32 bf16 MFMAs; X supplies the same K offsets. S is kept outside the
+// group's sum: the group's fp32 partial is multiplied by S[n, group] and accumulated, which
+// keeps every product exact (S q would need up to 14 significant bits). The waves' sums
+// meet in LDS. M above 128 is processed in slices of 128 rows (each re-reads W).
+#include "common.h"
+#include "internal.h"
+
+namespace w8a8 {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kG = 128;                 // group size along K
+constexpr int kGB = kG / 2;             // code bytes per row and group
+
+// ----------------------------------------------------------------------- quantization
+__global__ __launch_bounds__(256) void quant_int4_kernel(const u32x4* __restrict__ x, int64_t nthr,
+                                                         uint32_t* __restrict__ q,
+                                                         uint16_t* __restrict__ sc) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 32 elements per thread
+  const bool live = c < nthr;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = live ? __builtin_nontemporal_load(x + 4 * c + i) : u32x4{0u, 0u, 0u, 0u};
+  float amax = fmaxf(fmaxf(chunk_absmax(v[0]), chunk_absmax(v[1])), fmaxf(chunk_absmax(v[2]), chunk_absmax(v[3])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  if (!live) return;
+  _Float16 s16 = (_Float16)(amax / 7.0f);                      // IEEE division, then RNE to fp16
+  if (__builtin_isinf((float)s16)) s16 = (_Float16)65504.0f;
+  if ((float)s16 == 0.f) s16 = (_Float16)1.0f;
+  const float s = (float)s16;
+  const float rcp = 1.0f / s;                                  // s in [2^-24, 65504]: exact quotient
+  uint32_t out[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = __builtin_rintf(div_static(bf16_lo(w[e]), s, rcp));
+      const float hi = __builtin_rintf(div_static(bf16_hi(w[e]), s, rcp));
+      const int ql = (int)fminf(fmaxf(lo, -7.f), 7.f), qh = (int)fminf(fmaxf(hi, -7.f), 7.f);
+      out[i] |= ((uint32_t)(ql & 15) | ((uint32_t)(qh & 15) << 4)) << (8 * e);
+    }
+  }
+  reinterpret_cast<u32x4*>(q)[c] = u32x4{out[0], out[1], out[2], out[3]};
+  if ((threadIdx.x & 3) == 0) sc[c >> 2] = __builtin_bit_cast(uint16_t, s16);
+}
+
+// ------------------------------------------------------------------------------- GEMM
+// Eight 4-bit two's-complement codes (one word, element 2i in the low nibble of byte i) as
+// eight bf16 (exact).
+__device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
+  float f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = (float)((int)(w << (28 - 4 * e)) >> 28);
+  const uint32_t p0 = pack_bf16x2(f[0], f[1]), p1 = pack_bf16x2(f[2], f[3]);
+  const uint32_t p2 = pack_bf16x2(f[4], f[5]), p3 = pack_bf16x2(f[6], f[7]);
+  return __builtin_bit_cast(bf16x8, u32x4{p0, p1, p2, p3});
+}
+
+template <int MT, int WPB, int NW>
+__global__ void __launch_bounds__(WPB * 64)
+gemm_w4a16_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+                  const uint16_t* __restrict__ sc, int M, int N, int K, int groups,
+                  uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) f32x4 red[WPB][NW][MT][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fr = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16 * NW;
+  const int64_t kb = K / 2;
+
+  const uint8_t* wrow[NW];
+  const uint16_t* srow[NW][4];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    wrow[j] = wq + (int64_t)min(n0 + 16 * j + fr, N - 1) * kb + 16 * g;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) srow[j][r] = sc + (int64_t)min(n0 + 16 * j + 4 * g + r, N - 1) * groups;
+  }
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) xrow[i] = x + (int64_t)min(16 * i + fr, M - 1) * K + 32 * g;
+
+  f32x4 acc[NW][MT];
+#pragma unroll
+  for (int j = 0; j < NW; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Groups of this wave: gi = wave + WPB * s for s < cnt. Weights (and scales) one group
+  // ahead, X loaded with the group; loads past the last group re-read it (in bounds, never
+  // accumulated).
+  const int cnt = (groups - wave + WPB - 1) / WPB;
+  auto gidx = [&](int s) { return wave + WPB * min(s, cnt - 1); };
+  u32x4 wn[NW];
+  float sn[NW][4];
+  auto load_w = [&](int s) {
+    const int gi = gidx(s);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      wn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + (int64_t)gi * kGB));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sn[j][r] = (float)__builtin_bit_cast(_Float16, srow[j][r][gi]);
+    }
+  };
+  if (cnt > 0) load_w(0);
+  for (int s = 0; s < cnt; ++s) {
+    const int gi = gidx(s);
+    u32x4 wc[NW];
+    float scur[NW][4];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      wc[j] = wn[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) scur[j][r] = sn[j][r];
+    }
+    u32x4 xv[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        xv[i][p] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)gi * kG + 8 * p);
+    if (s + 1 < cnt) load_w(s + 1);
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const uint32_t ww[4] = {wc[j].x, wc[j].y, wc[j].z, wc[j].w};
+      bf16x8 wf[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) wf[p] = int4x8_to_bf16(ww[p]);
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[p], __builtin_bit_cast(bf16x8, xv[i][p]), part, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[r], scur[j][r], acc[j][i][r]);
+      }
+    }
+  }
+
+  // Partial sums of the waves meet in LDS. Lane l holds output row m = 16 i + (l & 15) and
+  // the four consecutive columns n0 + 16 j + 4 (l >> 4) + r.
+#pragma unroll
+  for (int j = 0; j < NW; ++j)
+#pragma unroll
+    for (int i = 0; i < MT; ++i) red[wave][j][i][lane] = acc[j][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < NW * MT * 64; idx += WPB * 64) {
+    const int j = idx / (MT * 64), i = (idx >> 6) % MT, l = idx & 63;
+    f32x4 v = red[0][j][i][l];
+#pragma unroll
+    for (int w = 1; w < WPB; ++w) v += red[w][j][i][l];
+    const int m = 16 * i + (l & 15), n = n0 + 16 * j + 4 * (l >> 4);
+    if (m >= M || n >= N) continue;
+    uint16_t* yr = y + (int64_t)m * N;
+    const uint32_t o[2] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    if ((N & 3) == 0) {
+      *reinterpret_cast<u32x2*>(yr + n) = u32x2{o[0], o[1]};
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (n + r < N) yr[n + r] = (uint16_t)((o[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+    }
+  }
+}
+
+template <int MT, int WPB, int NW>
+hipError_t launch_w4a16_cfg(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
+                            int64_t K, void* y, hipStream_t st) {
+  const int blocks = (int)((N + 16 * NW - 1) / (16 * NW));
+  hipLaunchKernelGGL((gemm_w4a16_kernel<MT, WPB, NW>), dim3((unsigned)blocks), dim3(WPB * 64), 0, st,
+                     (const uint16_t*)x, (const uint8_t*)wq, sc, (int)M, (int)N, (int)K, (int)(K / kG),
+                     (uint16_t*)y);
+  return hipGetLastError();
+}
+
+// Launch shape by token count (MT 16-row subtiles) and layer width, for M <= 128.
+hipError_t launch_w4a16_slice(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
+                              int64_t K, void* y, hipStream_t st) {
+  const bool wide = N > 8192;
+  if (M <= 16) return wide ? launch_w4a16_cfg<1, 8, 2>(x, wq, sc, M, N, K, y, st)
+                           : launch_w4a16_cfg<1, 8, 1>(x, wq, sc, M, N, K, y, st);
+  if (M <= 32) return launch_w4a16_cfg<2, 8, 1>(x, wq, sc, M, N, K, y, st);
+  if (M <= 64) return launch_w4a16_cfg<4, 4, 1>(x, wq, sc, M, N, K, y, st);
+  return launch_w4a16_cfg<8, 4, 1>(x, wq, sc, M, N, K, y, st);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, uint16_t* sc,
+                                hipStream_t st) {
+  const int64_t nthr = N * K / 32;
+  hipLaunchKernelGGL(quant_int4_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const u32x4*>(w), nthr, reinterpret_cast<uint32_t*>(q), sc);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
+                             int64_t K, void* y, hipStream_t st) {
+  for (int64_t m0 = 0; m0 < M; m0 += 128) {
+    const int64_t mr = M - m0 < 128 ? M - m0 : 128;
+    const hipError_t e = launch_w4a16_slice(reinterpret_cast<const uint16_t*>(x) + m0 * K, wq, sc, mr,
+                                            N, K, reinterpret_cast<uint16_t*>(y) + m0 * N, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace w8a8

@@ -1,5 +1,6 @@
 /*
- * w8a8.h - C ABI of the MI355X (gfx950) W8A8 / block-scaled FP8 / INT8 / MXFP4 / NVFP4 library.
+ * w8a8.h - C ABI of the MI355X (gfx950) W8A8 / block-scaled FP8 / INT8 / MXFP4 / NVFP4 / W4A16
+ * library.
  *
  * The calls follow the problem statement of three pages:
  *   [P-FP8FP4]  "FP8 and FP4 inference, SmoothQuant and activation quantization"
@@ -240,6 +241,27 @@ w8a8_status w8a8_quantize_nvfp4(const void* x_bf16, int64_t R, int64_t K, int sc
 w8a8_status w8a8_gemm_nvfp4(const void* xq, const uint8_t* sx, const float* gx, const void* wq,
                             const uint8_t* sw, const float* gw, int64_t M, int64_t N, int64_t K,
                             void* y_bf16, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * W4A16 weight-only decode path ([P-LOWBIT] §2.3: symmetric INT4, q in [-7, 7],
+ * S = max|x| / 7 per group of 128 along K, 2 bytes of scale per group; §3.3: weights
+ * unpacked and dequantized next to a 16-bit product, activations stay 16-bit).
+ *
+ * Quantize a bf16 weight matrix [N, K] per group of 128 along K:
+ *   S = fp16_rne(fp32(amax) / 7) (1 for an all-zero group; 65504 where fp16 overflows);
+ *   q = clamp(rint_half_even(x / S), -7, 7) with the IEEE fp32 quotient.
+ *   q_packed: [N, K/2] bytes, 4-bit two's complement, element 2i in the low nibble.
+ *   scale_f16: [N, K/128] IEEE fp16.    K % 128 == 0.
+ */
+w8a8_status w8a8_quantize_int4(const void* w_bf16, int64_t N, int64_t K, void* q_packed,
+                               uint16_t* scale_f16, void* stream);
+
+/* W4A16 GEMM: y[m,n] = bf16_rne( sum_g S[n,g] sum_{k in g} x[m,k] q[n,k] ), x bf16 [M, K],
+ * FP32 accumulation on the bf16 matrix cores (the INT4 codes are exact in bf16, S is applied
+ * to each group's partial sum). Built for decode (small M): W is streamed once per 128 rows
+ * of M. K % 128 == 0. */
+w8a8_status w8a8_gemm_w4a16(const void* x_bf16, const void* q_packed, const uint16_t* scale_f16,
+                            int64_t M, int64_t N, int64_t K, void* y_bf16, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * SmoothQuant preparation for the INT8 variant ([P-FP8FP4] "SmoothQuant: move the

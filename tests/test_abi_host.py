@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
               "w8a8_quantize_per_token_group", "w8a8_quantize_weight_block", "w8a8_gemm_blockscaled",
               "w8a8_quantize_mxfp4", "w8a8_gemm_mxfp4", "w8a8_channel_absmax",
               "w8a8_smoothquant_scales", "w8a8_smooth_apply", "w8a8_status_string",
-              "w8a8_quantize_nvfp4", "w8a8_gemm_nvfp4"]:
+              "w8a8_quantize_nvfp4", "w8a8_gemm_nvfp4", "w8a8_quantize_int4", "w8a8_gemm_w4a16"]:
         assert n in names
 
 
@@ -159,6 +159,18 @@ def test_nvfp4_validation(L):
     assert gn(A, A, A, A, A, 0x10002, 4, 4, 64, A, None) == EALIGN
     assert gn(A, MIS, A, A, A, A, 4, 4, 64, A, None) == EALIGN
     assert gn(A, A, A, A, A, A, 0, 4, 64, A, None) == OK
+
+
+def test_w4a16_validation(L):
+    assert L.w8a8_quantize_int4(A, 4, 64, A, A, None) == EUNSUP        # K % 128
+    assert L.w8a8_quantize_int4(A, 4, 128, None, A, None) == ENULL
+    assert L.w8a8_quantize_int4(A, 4, 128, A, MIS, None) == EALIGN
+    assert L.w8a8_quantize_int4(None, 0, 128, None, None, None) == OK
+    assert L.w8a8_gemm_w4a16(A, A, A, 1, 4, 64, A, None) == EUNSUP
+    assert L.w8a8_gemm_w4a16(A, A, None, 1, 4, 128, A, None) == ENULL
+    assert L.w8a8_gemm_w4a16(A, A, A, 1, 4, 128, MIS, None) == EALIGN
+    assert L.w8a8_gemm_w4a16(A, A, A, -1, 4, 128, A, None) == ESHAPE
+    assert L.w8a8_gemm_w4a16(None, None, None, 0, 4, 128, None, None) == OK
 
 
 def test_smoothquant_validation(L):

@@ -1,0 +1,95 @@
+"""GPU parity: W4A16 (symmetric INT4, one fp16 scale per 128 along K) quantization bit for
+bit, and the weight-only GEMM within |y - y_ref| <= 1e-2 (|y_ref| + rms(y_ref)), against the
+oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+import fp4_w8a8_quantized_amd as w8
+from oracle import gemm as G
+from oracle import w4a16 as W
+from tests.gpu_util import bf16_to_f64, bits_u8, first_mismatch, need_gpu, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+def _bf16(v):
+    return synthetic.to_bf16_bits(np.asarray(v, np.float64))
+
+
+def _f16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _check_quant(wb, q, s, what):
+    oq, os_ = W.quantize_int4_groups(wb)
+    assert np.array_equal(_f16_bits(s), os_.view(np.uint16)), f"{what}: scales {first_mismatch(_f16_bits(s), os_.view(np.uint16))}"
+    assert np.array_equal(bits_u8(q), oq), f"{what}: codes {first_mismatch(bits_u8(q), oq)}"
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (300, 1024), (4096, 4096)])
+def test_quantize_int4(N, K):
+    need_gpu()
+    rng = np.random.default_rng(N + K)
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02 * np.exp2(rng.uniform(-6, 6, (N, 1))))
+    q, s = w8.quantize_int4(to_dev_bf16(wb))
+    torch.cuda.synchronize()
+    _check_quant(wb, q, s, f"{N}x{K}")
+
+
+def test_quantize_int4_special_groups():
+    need_gpu()
+    v = np.zeros((3, 512))
+    v[0, 128:256] = 1e6                      # fp16 scale saturates at 65504
+    v[1, :128] = [7.0, -3.5, 1.75, 0.5, -0.75, 2.5, -7.0] + [0.0] * 121
+    v[1, 128:256] = 1e-30                    # scale underflows fp16 -> 0 -> 1
+    v[2] = np.random.default_rng(2).standard_normal(512) * 3e4
+    v[2, 300] = -0.0
+    wb = _bf16(v)
+    q, s = w8.quantize_int4(to_dev_bf16(wb))
+    torch.cuda.synchronize()
+    _check_quant(wb, q, s, "special groups")
+
+
+def _gemm_compare(xb, wb, what):
+    q, s = w8.quantize_int4(to_dev_bf16(wb))
+    y = w8.gemm_w4a16(to_dev_bf16(xb), q, s)
+    torch.cuda.synchronize()
+    oq, os_ = W.quantize_int4_groups(wb)
+    assert np.array_equal(bits_u8(q), oq) and np.array_equal(_f16_bits(s), os_.view(np.uint16))
+    ok, worst = G.within_tolerance(bf16_to_f64(y), W.gemm_w4a16_ref(xb, oq, os_), TOL)
+    assert ok, f"{what}: worst error / bound = {worst:.3f}"
+
+
+# every 16-row subtile edge, M above 128 (slices), N not a multiple of 4 or 16, one group
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 7, 256), (16, 130, 384), (17, 64, 1024),
+                                   (33, 300, 512), (64, 4099, 256), (100, 96, 2048), (128, 257, 640),
+                                   (129, 33, 256), (300, 200, 384), (2, 9000, 1152)])
+def test_gemm_w4a16_ragged(M, N, K):
+    need_gpu()
+    rng = np.random.default_rng(M * 13 + N * 3 + K)
+    xb = _bf16(rng.standard_normal((M, K)))
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02)
+    _gemm_compare(xb, wb, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("N", synthetic.DECODE_NS)
+def test_gemm_w4a16_decode_sweep(N):
+    """The decode sweep's shapes (M in 1, 8, 32, 128; K = 4096) on its activations."""
+    need_gpu()
+    x_all = synthetic.decode_x()
+    wb = synthetic.decode_w(N)
+    q, s = w8.quantize_int4(to_dev_bf16(wb))
+    oq, os_ = W.quantize_int4_groups(wb)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_u8(q), oq) and np.array_equal(_f16_bits(s), os_.view(np.uint16))
+    for M in (1, 8, 32, 128):
+        xb = x_all[:M]
+        y = w8.gemm_w4a16(to_dev_bf16(xb), q, s)
+        torch.cuda.synchronize()
+        ok, worst = G.within_tolerance(bf16_to_f64(y), W.gemm_w4a16_ref(xb, oq, os_), TOL)
+        assert ok, f"M={M} N={N}: worst error / bound = {worst:.3f}"
