@@ -18,6 +18,9 @@ Other workloads (`--workload decode|blockscaled|mxfp4|all`) print one JSON line 
   blockscaled  M = 4096, K = 7168, N = 18432 with 1x128 activation groups and 128x128
                weight blocks (group quantize + block-scaled GEMM timed).
   mxfp4        M = N = K = 8192, MXFP4 operands (MX quantize of X + FP4 GEMM timed).
+  w4a16        weight-only INT4 (G = 128, fp16 scales) decode GEMM on bf16 activations,
+               M in {1,8,32,128}, K = 4096, N in {4096, 14336}; weights rotated over
+               >512 MB of copies.
   nvfp4        the same 8192^3 inputs as NVFP4 (tensor-scale pass + quantize of X, and the
                GEMM on the fp16 matrix cores, timed).
   epilogue     the prefill linears with the full epilogue: + bf16 bias, SiLU, and FP8
@@ -57,7 +60,7 @@ def _parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "blockscaled", "mxfp4", "nvfp4", "epilogue", "static", "all"])
+                   choices=["prefill", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16", "epilogue", "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=256,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
@@ -529,6 +532,79 @@ def run_decode(args, c: Ctx):
     return rec
 
 
+# ----------------------------------------------------------------------------- W4A16
+def run_w4a16(args, c: Ctx):
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh, stream = c.torch, c.w8, c.L, c.sh, c.stream
+    K = synthetic.DECODE_K
+    xall = c.bf16(synthetic.decode_x())
+    cases = []
+    for N in synthetic.DECODE_NS:
+        w = c.bf16(synthetic.decode_w(N))
+        q, s = w8.quantize_int4(w)
+        del w
+        wbytes = N * K // 2 + N * (K // 128) * 2
+        copies = max(2, math.ceil(600e6 / wbytes))
+        qs = [q] + [q.clone() for _ in range(copies - 1)]
+        ss = [s] + [s.clone() for _ in range(copies - 1)]
+        torch.cuda.synchronize()
+        for M in (1, 8, 32, 128):
+            x = xall[:M]
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+
+            def launch(i):
+                c.check(L.w8a8_gemm_w4a16(x.data_ptr(), qs[i % copies].data_ptr(), ss[i % copies].data_ptr(),
+                                          M, N, K, y.data_ptr(), sh))
+
+            for i in range(max(args.warmup, 3)):
+                launch(i)
+            R = 3 * copies
+            ev = [(c.event(), c.event()) for _ in range(R)]
+            torch.cuda.synchronize()
+            for i in range(R):
+                ev[i][0].record(stream)
+                launch(i)
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            g_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+            byt = wbytes + 2 * M * K + 2 * M * N
+            flops = 2.0 * M * N * K
+            cases.append({"M": M, "N": N, "gemm_us": round(g_us, 2), "gemm_GBps": round(byt / g_us / 1e3, 1),
+                          "gemm_tflops": round(flops / g_us / 1e6, 3),
+                          "hbm_frac": round(byt / g_us / 1e3 / HBM_PEAK_GBPS, 4)})
+        del qs, ss
+        torch.cuda.empty_cache()
+    tot_bytes = sum(cs["gemm_GBps"] * cs["gemm_us"] * 1e3 for cs in cases)
+    tot_us = sum(cs["gemm_us"] for cs in cases)
+    achieved = tot_bytes / tot_us / 1e3
+    rec = _base_record(
+        args, "W4A16 decode GEMM HBM GB/s (INT4 G=128 weights, bf16 activations, M<=128, K=4096, "
+              "N in {4096,14336})", achieved, "GB/s", tot_us / 1e3, "int4+bf16 (bf16 MFMA)",
+        {"workload": "weight-only INT4 decode sweep M in {1,8,32,128}, K=4096, N in {4096,14336}; "
+                     "weights rotated over >512 MB of copies", "K": K})
+    rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
+    rec["cases"] = cases
+    if not args.no_cpu_baseline:
+        from oracle import w4a16 as W4
+        wb = synthetic.decode_w(4096)
+        oq, os_ = W4.quantize_int4_groups(wb)
+        xb = synthetic.decode_x()[:32]
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 5.0:
+            np.asarray(W4.gemm_w4a16_ref(xb, oq, os_)).sum()
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        byt = 4096 * K // 2 + 4096 * (K // 128) * 2 + 2 * 32 * K + 2 * 32 * 4096
+        rec["cpu_baseline"] = {"value": round(byt / dt / 1e9, 3), "unit": "GB/s", "cores": _threads(),
+                               "kind": "oracle",
+                               "sample": f"M=32, N=4096, K={K} (dequantize + fp64 product), weights "
+                                         f"pre-quantized; {reps} runs of {dt:.2f} s"}
+    return rec
+
+
 # ----------------------------------------------------------------------------- block-scaled
 def _timed_pair(args, c: Ctx, first, second):
     """Warm up, then time `steps` of first() + second() with events around each."""
@@ -721,7 +797,7 @@ def main():
     c = Ctx()
     runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
             "epilogue": run_epilogue, "static": run_static,
-            "mxfp4": run_mxfp4, "nvfp4": run_nvfp4}
+            "mxfp4": run_mxfp4, "nvfp4": run_nvfp4, "w4a16": run_w4a16}
     names = list(runs) if args.workload == "all" else [args.workload]
     for name in names:
         rec = runs[name](args, c)
