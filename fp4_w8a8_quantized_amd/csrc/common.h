@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace w8a8 {
@@ -95,10 +96,34 @@ __device__ __forceinline__ float add_rn(float a, float b) {
 
 // GEMM epilogue activation: 0 identity, 1 ReLU max(v, 0), 2 SiLU v / (1 + e^-v) (with the
 // hardware exponential and reciprocal; SiLU is compared within a tolerance).
+template <int ACT>
+__device__ __forceinline__ float epi_act(float v) {
+  if constexpr (ACT == 1) return fmaxf(v, 0.f);
+  else if constexpr (ACT == 2) return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+  else return v;
+}
 __device__ __forceinline__ float epi_activate(float v, int act) {
-  if (act == 1) return fmaxf(v, 0.f);
-  if (act == 2) return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+  if (act == 1) return epi_act<1>(v);
+  if (act == 2) return epi_act<2>(v);
   return v;
+}
+
+// Calls f(integral_constant<int, act>, integral_constant<bool, bias>) once, so that an
+// epilogue's element loop is compiled per (activation, bias) with no branch inside it.
+template <class F>
+__device__ __forceinline__ void epi_dispatch(int act, bool bias, F&& f) {
+  using A0 = std::integral_constant<int, 0>;
+  using A1 = std::integral_constant<int, 1>;
+  using A2 = std::integral_constant<int, 2>;
+  if (bias) {
+    if (act == 1) f(A1{}, std::true_type{});
+    else if (act == 2) f(A2{}, std::true_type{});
+    else f(A0{}, std::true_type{});
+  } else {
+    if (act == 1) f(A1{}, std::false_type{});
+    else if (act == 2) f(A2{}, std::false_type{});
+    else f(A0{}, std::false_type{});
+  }
 }
 
 // clamp(q, +-448); a NaN stays NaN (both comparisons are false).

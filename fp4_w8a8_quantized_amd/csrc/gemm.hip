@@ -327,40 +327,54 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   lds_barrier();
+  // FP8 and INT8 tiles check bias and activation at run time (ACT = -1; one copy of the
+  // element loop keeps the widest INT8 tile within its registers); the block-scaled and
+  // MXFP4 GEMMs have no epilogue options, so their loop is compiled without the checks.
+  auto stage = [&](auto act_c, auto bias_c) {
+    constexpr int ACT = decltype(act_c)::value;
+    constexpr bool BIAS = decltype(bias_c)::value;
 #pragma unroll
-  for (int i = 0; i < SM; ++i) {
-    const int rl = xrow0 + SUB * i + fr;
+    for (int i = 0; i < SM; ++i) {
+      const int rl = xrow0 + SUB * i + fr;
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
+      for (int j = 0; j < SN; ++j) {
 #pragma unroll
-      for (int q = 0; q < NG; ++q) {
-        const int cl = wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g);
-        float v[4];
+        for (int q = 0; q < NG; ++q) {
+          const int cl = wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g);
+          float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const acc_e a = acc[j][i][4 * q + r];
-          if constexpr (KIND == KIND_FP8) {
-            v[r] = a * (esm[i] * esn[j][q][r]);
-          } else if constexpr (KIND == KIND_INT8) {
-            v[r] = mul_rn(mul_rn((float)a, esm[i]), esn[j][q][r]);
-          } else {
-            v[r] = a;
+          for (int r = 0; r < 4; ++r) {
+            const acc_e a = acc[j][i][4 * q + r];
+            if constexpr (KIND == KIND_FP8) {
+              v[r] = a * (esm[i] * esn[j][q][r]);
+            } else if constexpr (KIND == KIND_INT8) {
+              v[r] = mul_rn(mul_rn((float)a, esm[i]), esn[j][q][r]);
+            } else {
+              v[r] = a;
+            }
+            if constexpr (ACT < 0) {
+              if (has_bias) v[r] = add_rn(v[r], ebias[j][q][r]);
+              v[r] = epi_activate(v[r], ep.act);
+            } else {
+              if constexpr (BIAS) v[r] = add_rn(v[r], ebias[j][q][r]);
+              v[r] = epi_act<ACT>(v[r]);
+            }
           }
-          if (has_bias) v[r] = add_rn(v[r], ebias[j][q][r]);
-          v[r] = epi_activate(v[r], ep.act);
-        }
-        if constexpr (OF8) {
-          constexpr bool EX = (KIND == KIND_INT8);
-          *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
-              pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
-                          epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
-        } else {
-          const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+          if constexpr (OF8) {
+            constexpr bool EX = (KIND == KIND_INT8);
+            *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
+                pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
+                            epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
+          } else {
+            const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+          }
         }
       }
     }
-  }
+  };
+  if constexpr (SCALED) stage(std::integral_constant<int, -1>{}, std::false_type{});
+  else stage(std::integral_constant<int, 0>{}, std::false_type{});
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   lds_barrier();
   constexpr int EPC = 16 / ES;                 // output elements per 16-byte chunk

@@ -218,29 +218,33 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   pp_barrier();
   // In the 16x16 result (A = W fragment, B = X fragment), lane l holds output row
   // m = 16 i + (l & 15) and the four consecutive columns 16 j + 4 (l >> 4) + r.
+  epi_dispatch(ep.act, has_bias, [&](auto act_c, auto bias_c) {
+    constexpr int ACT = decltype(act_c)::value;
+    constexpr bool BIAS = decltype(bias_c)::value;
 #pragma unroll
-  for (int i = 0; i < SM; ++i) {
-    const int rl = xrow0 + 16 * i + fr;
+    for (int i = 0; i < SM; ++i) {
+      const int rl = xrow0 + 16 * i + fr;
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int cl = wrow0 + 16 * j + 4 * g;
-      float v[4];
+      for (int j = 0; j < SN; ++j) {
+        const int cl = wrow0 + 16 * j + 4 * g;
+        float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v[r] = acc[j][i][r] * (esm[i] * esn[j][r]);
-        if (has_bias) v[r] = add_rn(v[r], ebias[j][r]);
-        v[r] = epi_activate(v[r], ep.act);
-      }
-      if constexpr (OF8) {
-        *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
-            pack_e4m3x4(epi_requant<false>(v[0], ep.s_out, ep.inv_s_out), epi_requant<false>(v[1], ep.s_out, ep.inv_s_out),
-                        epi_requant<false>(v[2], ep.s_out, ep.inv_s_out), epi_requant<false>(v[3], ep.s_out, ep.inv_s_out));
-      } else {
-        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[j][i][r] * (esm[i] * esn[j][r]);
+          if constexpr (BIAS) v[r] = add_rn(v[r], ebias[j][r]);
+          v[r] = epi_act<ACT>(v[r]);
+        }
+        if constexpr (OF8) {
+          *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
+              pack_e4m3x4(epi_requant<false>(v[0], ep.s_out, ep.inv_s_out), epi_requant<false>(v[1], ep.s_out, ep.inv_s_out),
+                          epi_requant<false>(v[2], ep.s_out, ep.inv_s_out), epi_requant<false>(v[3], ep.s_out, ep.inv_s_out));
+        } else {
+          const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
+        }
       }
     }
-  }
+  });
   __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));
   pp_barrier();
   constexpr int EPC = 16 / ES;                         // output elements per 16-byte chunk

@@ -126,49 +126,54 @@ gemm_skinny_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 #pragma unroll
   for (int i = 0; i < MT; ++i) red[wave][j][i][lane] = acc[j][i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < NW * MT * 64; idx += WPB * 64) {
-    const int j = idx / (MT * 64), i = (idx >> 6) % MT, l = idx & 63;
-    acc_t s = red[0][j][i][l];
+  // The element loop is compiled per (activation, bias): no branch inside it.
+  epi_dispatch(ep.act, ep.bias != nullptr, [&](auto act_c, auto bias_c) {
+    constexpr int ACT = decltype(act_c)::value;
+    constexpr bool BIAS = decltype(bias_c)::value;
+    for (int idx = threadIdx.x; idx < NW * MT * 64; idx += WPB * 64) {
+      const int j = idx / (MT * 64), i = (idx >> 6) % MT, l = idx & 63;
+      acc_t s = red[0][j][i][l];
 #pragma unroll
-    for (int w = 1; w < WPB; ++w) s += red[w][j][i][l];
-    const int m = 16 * i + (l & 15), n = n0 + 16 * j + 4 * (l >> 4);
-    if (m >= M || n >= N) continue;
-    const float sm = sx[m];
-    float v[4];
+      for (int w = 1; w < WPB; ++w) s += red[w][j][i][l];
+      const int m = 16 * i + (l & 15), n = n0 + 16 * j + 4 * (l >> 4);
+      if (m >= M || n >= N) continue;
+      const float sm = sx[m];
+      float v[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int nn = min(n + r, N - 1);
-      const float swn = sw[nn];
-      if constexpr (KIND == 1) v[r] = mul_rn(mul_rn((float)s[r], sm), swn);
-      else v[r] = s[r] * (sm * swn);
-      if (ep.bias) v[r] = add_rn(v[r], bf16_lo(ep.bias[nn]));
-      v[r] = epi_activate(v[r], ep.act);
-    }
-    if constexpr (OF8) {
-      constexpr bool EX = (KIND == 1);
-      const uint32_t o = pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
-                                     epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
-      uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + (size_t)m * N;
-      if ((N & 3) == 0) {
-        *reinterpret_cast<uint32_t*>(yr + n) = o;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) yr[n + r] = (uint8_t)((o >> (8 * r)) & 0xFFu);
+      for (int r = 0; r < 4; ++r) {
+        const int nn = min(n + r, N - 1);
+        const float swn = sw[nn];
+        if constexpr (KIND == 1) v[r] = mul_rn(mul_rn((float)s[r], sm), swn);
+        else v[r] = s[r] * (sm * swn);
+        if constexpr (BIAS) v[r] = add_rn(v[r], bf16_lo(ep.bias[nn]));
+        v[r] = epi_act<ACT>(v[r]);
       }
-    } else {
-      uint16_t* yr = reinterpret_cast<uint16_t*>(yp) + (size_t)m * N;
-      if ((N & 3) == 0) {
-        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(yr + n) = o;
-      } else {
-        const uint32_t o[2] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      if constexpr (OF8) {
+        constexpr bool EX = (KIND == 1);
+        const uint32_t o = pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
+                                       epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
+        uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + (size_t)m * N;
+        if ((N & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(yr + n) = o;
+        } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (n + r < N) yr[n + r] = (uint16_t)((o[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) yr[n + r] = (uint8_t)((o >> (8 * r)) & 0xFFu);
+        }
+      } else {
+        uint16_t* yr = reinterpret_cast<uint16_t*>(yp) + (size_t)m * N;
+        if ((N & 3) == 0) {
+          const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(yr + n) = o;
+        } else {
+          const uint32_t o[2] = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) yr[n + r] = (uint16_t)((o[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+        }
       }
     }
-  }
+  });
 }
 
 template <int KIND, int MT, int WPB, int NW>
