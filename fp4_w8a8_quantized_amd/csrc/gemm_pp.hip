@@ -21,6 +21,7 @@
 // each B wave issues half of its loads of step k+2 into the stage, waits for its loads of
 // step k+1 (so the barrier that ends the slot publishes them to A), and issues the other
 // half between the MFMAs of its next phase. The stage is next read by A two slots later.
+// The last two steps load nothing and wait for all outstanding loads instead.
 //
 // Fragments: lane l reads row l & 15 and the 16-byte chunks g and g + 4 (g = l >> 4) of the
 // 128-byte K step; both operands permute K the same way, so every dot product still covers
@@ -151,6 +152,20 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
       }
   };
 
+  // The epilogue's scales (and biases) are loaded up front; their latency hides behind
+  // the K loop.
+  float esm[SM], esn[SN][4], ebias[SN][4];
+  const bool has_bias = ep.bias != nullptr;
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1);
+      esn[j][r] = sw[n];
+      ebias[j][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
+    }
+#pragma unroll
+  for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + 16 * i + fr, M - 1)];
   // Prologue: group B loads steps 0 and 1; step 0 landed and published. Past the last
   // step, loads re-fetch the last step into a stage nobody reads again (branch-free).
   if (grp == 1) {
@@ -176,22 +191,32 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     }
     pp_barrier();
   } else {
-    pp_barrier();                                      // slot 0
-    for (int ks = 0; ks < ksteps; ++ks) {
+    // Group B. The last two steps have nothing left to load: they wait for everything
+    // outstanding instead (no re-fetch of the last step into a stage nobody reads).
+    auto iter = [&](int ks, auto load_c) {
+      constexpr bool LOAD = decltype(load_c)::value;
       lds_phase(ks);                                   // slot 2k+1, first half
       __builtin_amdgcn_sched_barrier(0);
       pp_barrier();                                    // no wave reads stage ks & 1 any more
-      const int kd = min(ks + 2, ksteps - 1);
+      if constexpr (LOAD) {
 #pragma unroll
-      for (int d = 0; d < DMA - DC; ++d) dma_one(kd, ks & 1, d);
-      // Everything older than this slot's loads has landed: that is all of step k+1.
-      __builtin_amdgcn_s_waitcnt(pp_wait(DMA - DC, 15));
+        for (int d = 0; d < DMA - DC; ++d) dma_one(ks + 2, ks & 1, d);
+        // Everything older than this slot's loads has landed: that is all of step k+1.
+        __builtin_amdgcn_s_waitcnt(pp_wait(DMA - DC, 15));
+      } else {
+        __builtin_amdgcn_s_waitcnt(pp_wait(0, 15));
+      }
       __builtin_amdgcn_sched_barrier(0);
       pp_barrier();
-      mfma_phase_loading(kd, ks & 1);                  // slot 2k+2
+      if constexpr (LOAD) mfma_phase_loading(ks + 2, ks & 1);   // slot 2k+2
+      else mfma_range(0, T);
       __builtin_amdgcn_sched_barrier(0);
       pp_barrier();
-    }
+    };
+    pp_barrier();                                      // slot 0
+    int ks = 0;
+    for (; ks + 2 < ksteps; ++ks) iter(ks, std::true_type{});
+    for (; ks < ksteps; ++ks) iter(ks, std::false_type{});
   }
 
   // ---- epilogue. Every load has landed and every wave is past its last fragment read.
@@ -202,18 +227,6 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   auto opos = [&](int row, int byte) -> int {
     return SWZ ? row * RS + ((((byte >> 4) ^ (row & 15)) << 4) | (byte & 15)) : row * RS + byte;
   };
-  float esm[SM], esn[SN][4], ebias[SN][4];
-  const bool has_bias = ep.bias != nullptr;
-#pragma unroll
-  for (int j = 0; j < SN; ++j)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1);
-      esn[j][r] = sw[n];
-      ebias[j][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
-    }
-#pragma unroll
-  for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + 16 * i + fr, M - 1)];
   __builtin_amdgcn_s_waitcnt(pp_wait(0, 0));
   pp_barrier();
   // In the 16x16 result (A = W fragment, B = X fragment), lane l holds output row
@@ -249,11 +262,23 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   pp_barrier();
   constexpr int EPC = 16 / ES;                         // output elements per 16-byte chunk
   constexpr int CPR = BN / EPC;                        // chunks per output row
-  for (int c = t; c < BM * CPR; c += kPPThreads) {
+  // Every thread moves ITERS chunks: all LDS reads first, then all global stores.
+  constexpr int ITERS = BM * CPR / kPPThreads;
+  static_assert(ITERS * kPPThreads == BM * CPR, "whole chunks per thread");
+  u32x4 ov[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int c = t + it * kPPThreads;
+    const int rl = c / CPR, ch = c - rl * CPR;
+    ov[it] = *reinterpret_cast<const u32x4*>(lds + opos(rl, ch * 16));
+  }
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    const int c = t + it * kPPThreads;
     const int rl = c / CPR, ch = c - rl * CPR;
     const int m = m0 + rl, n = n0 + ch * EPC;
     if (m >= M || n >= N) continue;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + opos(rl, ch * 16));
+    const u32x4 v = ov[it];
     uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + ((size_t)m * N + n) * ES;
     if (vec_store && n + EPC - 1 < N) {
       *reinterpret_cast<u32x4*>(yr) = v;
