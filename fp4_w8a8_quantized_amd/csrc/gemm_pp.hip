@@ -7,8 +7,8 @@
 // and every direct-to-LDS load it issues sits between two MFMAs, and the CU's address
 // unit (about 64 B per clock) and LDS latency hold back the matrix core. Here a 512-thread
 // workgroup (8 waves, 2 per SIMD) computes a 256 x BN tile; each wave owns 128 x BN/4 of
-// it. Waves 0-3 (group A) and 4-7 (group B) alternate between two phases separated by
-// workgroup barriers:
+// it (64 x 64 at BN = 128). Waves 0-3 (group A) and 4-7 (group B) alternate between two
+// phases separated by workgroup barriers:
 //   LDS phase:  read this step's X and W fragments into registers
 //   MFMA phase: SM x SN MFMAs on them
 // so that while one wave of a SIMD issues memory instructions the other keeps the matrix
@@ -65,10 +65,14 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
                int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
   constexpr int BM = kPPBM;
-  constexpr int SM = 8;                       // 128 rows per wave, 16-row subtiles
-  constexpr int WC = BN / 4;                  // columns per wave
+  // Wave tiles: 128 x BN/4 (2 x 4 waves), or 64 x 64 at BN = 128 (4 x 2 waves), which reads
+  // 8 fragments per step instead of 10 for the same 64 accumulators.
+  constexpr int WAVES_M = (BN == 128) ? 4 : 2;
+  constexpr int WR = BM / WAVES_M;            // rows per wave
+  constexpr int SM = WR / 16;                 // 16-row subtiles
+  constexpr int WC = BN * WAVES_M / 8;        // columns per wave
   constexpr int SN = WC / 16;
-  static_assert(SN * 16 * 4 == BN, "tile width must give whole 16-column subtiles per wave");
+  static_assert(SN * 16 * (8 / WAVES_M) == BN, "tile width must give whole 16-column subtiles per wave");
   constexpr int XT = BM * 128, WT = BN * 128, STAGE = XT + WT;
   constexpr int XI = BM / 32, WI = BN / 32;   // 1 KB loads per group-B wave per step
   constexpr int DMA = XI + WI;
@@ -78,7 +82,8 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int grp = wave >> 2, g4 = wave & 3;
-  const int wm = g4 & 1, wn = grp * 2 + (g4 >> 1);
+  const int wm = WAVES_M == 4 ? g4 : (g4 & 1);
+  const int wn = WAVES_M == 4 ? grp : grp * 2 + (g4 >> 1);
   // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that consecutive tiles
   // (which share a W panel) run on one XCD and its L2.
   int b = blockIdx.x;
@@ -103,7 +108,7 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 
   const int fr = lane & 15, g = lane >> 4;
   const int fo0 = pp_off(fr, g), fo1 = pp_off(fr, g + 4);
-  const int xrow0 = wm * 128, wrow0 = wn * WC;
+  const int xrow0 = wm * WR, wrow0 = wn * WC;
   typedef int frag_t __attribute__((ext_vector_type(8)));
   auto frag = [&](const uint8_t* base) -> frag_t {
     const i32x4 a = *reinterpret_cast<const i32x4*>(base + fo0);
