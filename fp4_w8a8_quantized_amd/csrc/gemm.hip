@@ -1,21 +1,20 @@
-// Low-precision GEMMs with fused scale epilogues on gfx950 matrix cores.
+// The tiled GEMM for INT8 (SmoothQuant W8A8) and block-scaled FP8 on gfx950 matrix cores,
+// and the GEMM dispatch (few tokens: gemm_skinny.hip; FP8: gemm_pp.hip; MXFP4:
+// gemm_mx_pp.hip).
 //
-//   FP8    y = bf16( s_x[m] s_w[n] sum_k dec(xq) dec(wq) )      v_mfma_f32_16x16x128_f8f6f4
-//   BLOCK  y = bf16( sum_g s_x[m,g] s_w[n/128,g] partial_g )    same, one fp32 partial per 128-K group
+//   BLOCK  y = bf16( sum_g s_x[m,g] s_w[n/128,g] partial_g )    v_mfma_f32_16x16x128_f8f6f4, one fp32 partial per 128-K group
 //   INT8   y = bf16( fp32(fp32(acc_i32) s_x[m]) s_w[n] )        v_mfma_i32_32x32x32_i8
-//   MXFP4  y = bf16( sum_b 2^ex 2^ew sum dec4 dec4 )            v_mfma_scale_f32_32x32x64_f8f6f4
 //
 // The scales are applied after the low-precision reduction, which the scale-factoring
 // identity diag(s_X)(X_q W_q^T)diag(s_W) allows ("FP8 and FP4 inference, SmoothQuant and
 // activation quantization", Scale granularity; "FP8 and INT8 Inference" §6-9, the GEMM
 // epilogue; "Low-bit LLM Weights and Activations" §3.4). The block-scaled variant
 // promotes each 128-wide K group's fp32 partial into the running fp32 sum ("FP8 and INT8
-// Inference" §5, What DeepSeek did); MXFP4 lets the matrix core apply the E8M0 block
-// scales ("Low-bit LLM Weights and Activations" §2.4). INT8 and FP4 use the 32x32 MFMA
-// shapes, which run at twice the rate of their 16x16 forms on gfx950.
+// Inference" §5, What DeepSeek did). INT8 uses the 32x32 MFMA shape, which runs at twice
+// the rate of its 16x16 form on gfx950.
 //
 // One 256-thread workgroup (4 waves, 2 x 2) computes a 256 x BN output tile:
-//  - K advances 128 bytes per step (128 FP8/INT8 elements, 256 FP4 elements). The X
+//  - K advances 128 bytes (128 elements) per step. The X
 //    [256 x 128 B] and W [BN x 128 B] slices of a step land in an LDS stage by direct
 //    global->LDS loads (no register staging). STAGES buffers give the loads STAGES-1
 //    steps to land.
@@ -37,7 +36,7 @@
 
 namespace w8a8 {
 
-enum Kind : int { KIND_FP8 = 0, KIND_INT8 = 1, KIND_BLOCK = 2, KIND_MXFP4 = 3 };
+enum Kind : int { KIND_INT8 = 1, KIND_BLOCK = 2 };
 
 constexpr int kBM = 256;
 constexpr int kThreads = 256;
@@ -77,7 +76,7 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_wav
 gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
             const uint8_t* __restrict__ wq, const void* __restrict__ swp, int M, int N,
             int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
-  constexpr bool MF32 = (KIND == KIND_INT8 || KIND == KIND_MXFP4);
+  constexpr bool MF32 = (KIND == KIND_INT8);
   constexpr int SUB = MF32 ? 32 : 16;         // MFMA output tile edge
   constexpr int SM = 128 / SUB;               // X subtiles per wave (128 rows)
   constexpr int SN = (BN / 2) / SUB;          // W subtiles per wave (BN/2 rows)
@@ -154,7 +153,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
     for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{};
 
-  // Scale state (block-scaled: fp32 per row group and W block; MXFP4: E8M0 bytes).
+  // Scale state (block-scaled: fp32 per row group and W block).
   const int G = ksteps;
   int srow[SM], swrow[SN];
 #pragma unroll
@@ -162,8 +161,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
   for (int j = 0; j < SN; ++j) swrow[j] = min(n0 + wrow0 + SUB * j + fr, N - 1);
   float bsx[SM], bsw[SN];            // block-scaled: scales of the step being computed
-  u32x2 esx[SM], esw[SN];            // MXFP4: the 8 E8M0 bytes of the step being computed
-  auto load_scales = [&](int ks, float (&fx)[SM], float (&fw)[SN], u32x2 (&ex)[SM], u32x2 (&ew)[SN]) {
+  auto load_scales = [&](int ks, float (&fx)[SM], float (&fw)[SN]) {
     if constexpr (KIND == KIND_BLOCK) {
       const float* sx = reinterpret_cast<const float*>(sxp);
       const float* sw = reinterpret_cast<const float*>(swp);
@@ -173,22 +171,13 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
       for (int j = 0; j < SN; ++j)
         fw[j] = sw[(size_t)(min(n0 + wrow0 + SUB * j, N - 1) >> 7) * G + ks];
     }
-    if constexpr (KIND == KIND_MXFP4) {
-      const uint8_t* sx = reinterpret_cast<const uint8_t*>(sxp);
-      const uint8_t* sw = reinterpret_cast<const uint8_t*>(swp);
-      const int S = ksteps * 8;
-#pragma unroll
-      for (int i = 0; i < SM; ++i) ex[i] = *reinterpret_cast<const u32x2*>(sx + (size_t)srow[i] * S + ks * 8);
-#pragma unroll
-      for (int j = 0; j < SN; ++j) ew[j] = *reinterpret_cast<const u32x2*>(sw + (size_t)swrow[j] * S + ks * 8);
-    }
   };
 
   // ---- prologue: stages 0..STAGES-1 in flight, stage 0 published, F(0) in registers
   frag_t xf[SM], wf0[SN], wf1[SN];
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) dma(min(s, ksteps - 1), s);
-  load_scales(0, bsx, bsw, esx, esw);
+  load_scales(0, bsx, bsw);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 1) * DMA_PER_STEP, 15));
   lds_barrier();
 #pragma unroll
@@ -215,15 +204,8 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
       for (int j = 0; j < SN; ++j) pin(bsw[j]);
     }
-    if constexpr (KIND == KIND_MXFP4) {
-#pragma unroll
-      for (int i = 0; i < SM; ++i) pin(esx[i]);
-#pragma unroll
-      for (int j = 0; j < SN; ++j) pin(esw[j]);
-    }
     float nsx[SM], nsw[SN];
-    u32x2 nex[SM], new_[SN];
-    load_scales(min(ks + 1, ksteps - 1), nsx, nsw, nex, new_);
+    load_scales(min(ks + 1, ksteps - 1), nsx, nsw);
     const int kdma = min(ks + STAGES, ksteps - 1);
     const uint8_t* X = lds + ((ks + 1) % STAGES) * STAGE;
     const uint8_t* W = X + XT;
@@ -243,31 +225,17 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     for (int i = 0; i < SM; ++i) {
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
-        if constexpr (KIND == KIND_FP8) {
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
-        } else if constexpr (KIND == KIND_BLOCK) {
+        if constexpr (KIND == KIND_BLOCK) {
           const int t = i * SN + j;
           if (t >= PD) promote(t - PD);
           pp[t % PD] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);      // keep the promotion PD MFMAs behind
-        } else if constexpr (KIND == KIND_INT8) {
+        } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const i32x4 a = {wcur[j][4 * q], wcur[j][4 * q + 1], wcur[j][4 * q + 2], wcur[j][4 * q + 3]};
             const i32x4 bb = {xf[i][4 * q], xf[i][4 * q + 1], xf[i][4 * q + 2], xf[i][4 * q + 3]};
             acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bb, acc[j][i], 0, 0, 0);
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            // FP4 operands occupy the low 16 bytes of the operand registers. The lane's
-            // 32 elements form block 2q + h of the step, whose scale byte it supplies.
-            const i32x8 a = {wcur[j][4 * q], wcur[j][4 * q + 1], wcur[j][4 * q + 2], wcur[j][4 * q + 3], 0, 0, 0, 0};
-            const i32x8 bb = {xf[i][4 * q], xf[i][4 * q + 1], xf[i][4 * q + 2], xf[i][4 * q + 3], 0, 0, 0, 0};
-            const int blk = 2 * q + g;
-            const int ea = (int)((((blk < 4) ? esw[j].x : esw[j].y) >> (8 * (blk & 3))) & 0xFFu);
-            const int eb = (int)((((blk < 4) ? esx[i].x : esx[i].y) >> (8 * (blk & 3))) & 0xFFu);
-            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[j][i], 4, 4, 0, ea, 0, eb);
           }
         }
       }
@@ -282,9 +250,9 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
       for (int t = SM * SN - PD; t < SM * SN; ++t) promote(t);
     }
 #pragma unroll
-    for (int i = 0; i < SM; ++i) { bsx[i] = nsx[i]; esx[i] = nex[i]; }
+    for (int i = 0; i < SM; ++i) bsx[i] = nsx[i];
 #pragma unroll
-    for (int j = 0; j < SN; ++j) { bsw[j] = nsw[j]; esw[j] = new_[j]; }
+    for (int j = 0; j < SN; ++j) bsw[j] = nsw[j];
   };
   int ks = 0;
   for (; ks + 1 < ksteps; ks += 2) {
@@ -308,7 +276,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   // The per-row and per-column scales (and biases) this lane needs are loaded in one
   // batch, so their latencies overlap, before the first epilogue barrier.
   constexpr int NG = MF32 ? 4 : 1;            // runs of 4 columns per lane per subtile
-  constexpr bool SCALED = (KIND == KIND_FP8 || KIND == KIND_INT8);
+  constexpr bool SCALED = (KIND == KIND_INT8);
   float esm[SM], esn[SN][NG][4], ebias[SN][NG][4];
   const bool has_bias = ep.bias != nullptr;
 #pragma unroll
@@ -345,9 +313,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const acc_e a = acc[j][i][4 * q + r];
-            if constexpr (KIND == KIND_FP8) {
-              v[r] = a * (esm[i] * esn[j][q][r]);
-            } else if constexpr (KIND == KIND_INT8) {
+            if constexpr (KIND == KIND_INT8) {
               v[r] = mul_rn(mul_rn((float)a, esm[i]), esn[j][q][r]);
             } else {
               v[r] = a;
@@ -429,7 +395,7 @@ static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, cons
   return hipGetLastError();
 }
 
-// Tile widths per variant. 32x32 variants (INT8, MXFP4) need multiples of 64. The
+// Tile widths per variant. The 32x32 INT8 variant needs multiples of 64. The
 // block-scaled variant keeps a per-group partial and its scales in registers, so it
 // stops at 192; the scale-carrying variants use two stages so that one vmcnt(0) per step
 // also retires their scale loads.
@@ -463,17 +429,6 @@ hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* 
   switch (pick_bn(M, N, c, 2)) {
     case 192: return launch_bn<192, KIND_BLOCK, 2>(st, xq, sx, wq, sw, M, N, K, y);
     default: return launch_bn<128, KIND_BLOCK, 2>(st, xq, sx, wq, sw, M, N, K, y);
-  }
-}
-
-hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
-                             const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
-                             hipStream_t st) {
-  static const int c[3] = {256, 192, 128};
-  switch (pick_bn(M, N, c, 3)) {
-    case 256: return launch_bn<256, KIND_MXFP4, 2>(st, xq, sx, wq, sw, M, N, K / 2, y);
-    case 192: return launch_bn<192, KIND_MXFP4, 2>(st, xq, sx, wq, sw, M, N, K / 2, y);
-    default: return launch_bn<128, KIND_MXFP4, 2>(st, xq, sx, wq, sw, M, N, K / 2, y);
   }
 }
 
