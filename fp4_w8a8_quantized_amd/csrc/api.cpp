@@ -224,7 +224,7 @@ w8a8_status w8a8_gemm_w4a16(const void* x_bf16, const void* q_packed, const uint
                             int64_t M, int64_t N, int64_t K, void* y_bf16, void* stream) {
   if (M < 0 || N < 0 || K < 0) return W8A8_ERR_SHAPE;
   if (K == 0 || K % 128 != 0) return W8A8_ERR_UNSUPPORTED;
-  if (M > kMaxOperandBytes / (2 * K) || N > kMaxOperandBytes / K) return W8A8_ERR_SHAPE;
+  if (M > kMaxOperandBytes / (2 * K) || N > kMaxOperandBytes / (K / 2)) return W8A8_ERR_SHAPE;
   if (M > INT32_MAX / 2 || N > INT32_MAX / 2) return W8A8_ERR_SHAPE;
   if (M == 0 || N == 0) return W8A8_OK;
   if (!x_bf16 || !q_packed || !scale_f16 || !y_bf16) return W8A8_ERR_NULL;

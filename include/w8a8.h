@@ -28,6 +28,9 @@
  *  - Every argument check runs on the host before anything is enqueued. On a non-zero
  *    status nothing has been enqueued and no output has been written.
  *  - A dimension of 0 rows (M, N or R) is valid and enqueues nothing.
+ *  - No operand (codes, bf16 input) may exceed 2^31 bytes, and M, N < 2^30: the kernels
+ *    address one matrix with 32-bit byte offsets. Larger shapes return W8A8_ERR_SHAPE;
+ *    split them along M or N.
  *  - Non-finite inputs are outside the contract: the kernels do not fault on them, a
  *    NaN element encodes to a NaN code, and a scale computed from an infinite amax is
  *    infinite.
@@ -44,7 +47,7 @@ extern "C" {
 typedef enum {
   W8A8_OK = 0,
   W8A8_ERR_NULL = 1,        /* a required pointer is NULL                              */
-  W8A8_ERR_SHAPE = 2,       /* a dimension is negative, or a size overflows int64      */
+  W8A8_ERR_SHAPE = 2,       /* a dimension is negative, or an operand is too large     */
   W8A8_ERR_UNSUPPORTED = 3, /* K is not a multiple of the call's granule, bad format   */
   W8A8_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned                 */
   W8A8_ERR_HIP = 5,         /* the HIP runtime reported an error when enqueuing        */

@@ -19,11 +19,14 @@ ship no data; these draws stand in for them):
 * ``blockscaled`` M=4096, K=7168, N=18432; X i.i.d. Student-t (nu = 3); W ~ N(0, 0.02^2).
 * ``mxfp4``     M=N=K=8192; X ~ N(0,1) times 2^u per (row, 32-element block),
                 u ~ U(-8, 8); W ~ N(0, 0.02^2).
+* ``random_bytes`` raw uniform bytes (seeded like the rest, workload index 9), shaped into
+                operand codes by the tests at the library's largest operand size.
 
-Seeds: workload index c (tiny 1, prefill 2, decode 3, blockscaled 4, mxfp4 5) and shape
-index i give base = 1000 c + 100 i; X uses base+1, W base+2, outlier channels base+3,
-the calibration draw base+4. Draws are fp64 from ``numpy.random.default_rng`` (PCG64),
-rounded to fp32 and then to bfloat16 with round-to-nearest-even.
+Seeds: workload index c (tiny 1, prefill 2, decode 3, blockscaled 4, mxfp4 5, largest
+operands 9) and shape index i give base = 1000 c + 100 i; X uses base+1, W base+2,
+outlier channels base+3, the calibration draw base+4. Draws are fp64 from
+``numpy.random.default_rng`` (PCG64), rounded to fp32 and then to bfloat16 with
+round-to-nearest-even.
 """
 
 from __future__ import annotations
@@ -131,3 +134,9 @@ def mxfp4(M: int = MXFP4_SHAPE[0], K: int = MXFP4_SHAPE[1], N: int = MXFP4_SHAPE
 def random_bf16(shape, s: int, scale: float = 1.0) -> np.ndarray:
     """Plain N(0, scale^2) bf16 draw for edge-case tests."""
     return to_bf16_bits(np.random.default_rng(s).standard_normal(shape) * scale)
+
+
+def random_bytes(n: int, s: int) -> np.ndarray:
+    """n uniform random bytes (writable uint8), for operand codes too large to build by
+    quantizing a bf16 draw (the largest operand the library accepts is 2^31 bytes)."""
+    return np.random.default_rng(s).integers(0, 256, size=n, dtype=np.uint8)

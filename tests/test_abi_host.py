@@ -190,3 +190,19 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros((4, 128), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         w8.quantize_per_token(x)
+
+
+def test_operand_byte_limit(L):
+    """One row past 2^31 bytes of any operand is a shape error, checked before launch."""
+    lim = 1 << 31
+    K = 16384
+    assert L.w8a8_gemm(A, A, A, A, 4, lim // K + 1, K, 0, A, None) == ESHAPE
+    assert L.w8a8_gemm(A, A, A, A, lim // K + 1, 4, K, 1, A, None) == ESHAPE
+    assert L.w8a8_gemm_blockscaled(A, A, A, A, 4, lim // K + 1, K, A, None) == ESHAPE
+    K = 32768
+    assert L.w8a8_gemm_mxfp4(A, A, A, A, 4, lim // (K // 2) + 1, K, A, None) == ESHAPE
+    assert L.w8a8_gemm_nvfp4(A, A, A, A, A, A, 4, lim // (K // 2) + 1, K, A, None) == ESHAPE
+    assert L.w8a8_gemm_w4a16(A, A, A, 4, lim // (K // 2) + 1, K, A, None) == ESHAPE
+    assert L.w8a8_gemm_w4a16(A, A, A, lim // (2 * K) + 1, 4, K, A, None) == ESHAPE
+    assert L.w8a8_quantize_per_token(A, lim // (2 * K) + 1, K, 0, A, A, None) == ESHAPE
+    assert L.w8a8_quantize_int4(A, lim // (2 * K) + 1, K, A, A, None) == ESHAPE
