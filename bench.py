@@ -102,16 +102,22 @@ def measured_traffic():
 
 
 def _counter_rows(path):
-    """(kernel name, counter value) per dispatch from a rocprofv3 counter_collection.csv."""
+    """(kernel name, counter value) per dispatch, in dispatch order, from a rocprofv3
+    counter_collection.csv."""
     import csv
     rows = []
     with open(path) as f:
         for r in csv.DictReader(f):
             name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
             val = r.get("Counter_Value") or r.get("Counter-Value")
+            did = r.get("Dispatch_Id") or r.get("Dispatch-Id") or len(rows)
             if val is not None:
-                rows.append((name, float(val)))
-    return rows
+                rows.append((int(did), name, float(val)))
+    return [(n, v) for _, n, v in sorted(rows)]
+
+
+# the counter passes run `--steps 2 --warmup 1`: GEMM dispatches 4..11 are the two timed steps
+TRAFFIC_STEPS, TRAFFIC_WARMUP = 2, 1
 
 
 def traffic_summary(args):
@@ -119,6 +125,7 @@ def traffic_summary(args):
     (KiB per dispatch), each scaled by what the same counter reports for a plain copy of
     args.copy_mib MiB (which moves exactly that many bytes each way)."""
     import numpy as np
+    import synthetic
     cf, cw, gf, gw = args.traffic_summary
     copy_bytes = args.copy_mib * 2**20
 
@@ -127,7 +134,9 @@ def traffic_summary(args):
         return float(np.median(v)) if v else float("nan")
 
     def gemm_kib(path):
+        nl = len(synthetic.PREFILL_SHAPES)
         v = [x for n, x in _counter_rows(path) if "gemm_pp_kernel" in n]
+        v = v[nl * TRAFFIC_WARMUP: nl * (TRAFFIC_WARMUP + TRAFFIC_STEPS)]   # the timed steps
         return float(np.mean(v)), len(v)
 
     f_scale = copy_bytes / (copy_kib(cf) * 1024.0)
@@ -136,17 +145,16 @@ def traffic_summary(args):
     wk, nw = gemm_kib(gw)
     fetch = fk * 1024.0 * f_scale
     write = wk * 1024.0 * w_scale
-    import synthetic
     alg = np.mean([2048 * K + N * K + 2 * 2048 * N for _, K, N in synthetic.PREFILL_SHAPES])
     text = f"""# HBM traffic of the FP8 GEMM in the 8B prefill step (mean per launch over QKV, O, gate+up, down)
 # commands (from the repository root, on one MI355X; each --pmc pass in a run of its own):
 #   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_copy_fetch -o copy -- python3 bench.py --calibrate-copy {args.copy_mib}
 #   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_copy_write -o copy -- python3 bench.py --calibrate-copy {args.copy_mib}
-#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_gemm_fetch -o gemm -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
-#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_gemm_write -o gemm -- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline
+#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_gemm_fetch -o gemm -- python3 bench.py --steps {TRAFFIC_STEPS} --warmup {TRAFFIC_WARMUP} --no-cpu-baseline
+#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_gemm_write -o gemm -- python3 bench.py --steps {TRAFFIC_STEPS} --warmup {TRAFFIC_WARMUP} --no-cpu-baseline
 #   python3 bench.py --traffic-summary <the four counter_collection.csv files> (this file)
 # copy calibration ({args.copy_mib} MiB each way): FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}
-# GEMM dispatches: {nf} (FETCH_SIZE pass), {nw} (WRITE_SIZE pass)
+# GEMM dispatches averaged: the {nf} (FETCH_SIZE pass) and {nw} (WRITE_SIZE pass) of the timed steps
 # algorithmic bytes per launch (MK + NK + 2MN, mean over the four shapes): {alg:.0f}
 gemm_source_sha256_16 = {gemm_source_hash()}
 fetch_bytes_per_launch = {fetch:.0f}
@@ -198,6 +206,20 @@ def _base_record(args, metric, value, unit, ms_per_step, dtype, config, higher=T
             "data": "synthetic", "config": config}
 
 
+def _launch_mean_s(c: Ctx, fn, reps: int) -> float:
+    """Mean duration in seconds of fn(0) .. fn(reps - 1), launched back to back on the bench
+    stream between one pair of HIP events. An event recorded between two launches costs a
+    gap and a cache flush that the measured kernel would then carry, so none is."""
+    e0, e1 = c.event(), c.event()
+    c.torch.cuda.synchronize()
+    e0.record(c.stream)
+    for i in range(reps):
+        fn(i)
+    e1.record(c.stream)
+    c.torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
 # ----------------------------------------------------------------------------- prefill
 def prefill_cpu_baseline(layers, rows: int):
     """The oracle as it stands on a sample of the same step: `rows` tokens of each linear
@@ -244,34 +266,33 @@ def run_prefill(args, c: Ctx):
         dl.append(dict(name=name, x=x, xq=xq, sx=sx, wq=wq, sw=sw, y=y, M=M, N=N, K=K))
     torch.cuda.synchronize()
 
-    def launch_layer(d):
+    def quant(d):
         c.check(L.w8a8_quantize_per_token(d["x"].data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
                                           d["sx"].data_ptr(), sh))
-        c.check(L.w8a8_gemm(d["xq"].data_ptr(), d["sx"].data_ptr(), d["wq"].data_ptr(),
+
+    def gemm(d, wq):
+        c.check(L.w8a8_gemm(d["xq"].data_ptr(), d["sx"].data_ptr(), wq.data_ptr(),
                             d["sw"].data_ptr(), d["M"], d["N"], d["K"], 0, d["y"].data_ptr(), sh))
 
+    # weight copies for the per-kernel passes below: at least 600 MB and 10 launches per layer
+    copies = []
+    for d in dl:
+        n = max(10, math.ceil(600e6 / (d["N"] * d["K"])))
+        copies.append([d["wq"]] + [d["wq"].clone() for _ in range(n - 1)])
     for _ in range(args.warmup):
         for d in dl:
-            launch_layer(d)
+            quant(d)
+            gemm(d, d["wq"])
     torch.cuda.synchronize()
 
-    # timed region: K steps, with HIP events around every launch on the launch stream
+    # timed region: K whole steps and nothing else on the stream
     nl = len(dl)
-    ev = [[(c.event(), c.event(), c.event()) for _ in range(nl)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        for li, d in enumerate(dl):
-            e0, e1, e2 = ev[s][li]
-            e0.record(stream)
-            st = L.w8a8_quantize_per_token(d["x"].data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
-                                           d["sx"].data_ptr(), sh)
-            assert st == 0
-            e1.record(stream)
-            st = L.w8a8_gemm(d["xq"].data_ptr(), d["sx"].data_ptr(), d["wq"].data_ptr(),
-                             d["sw"].data_ptr(), d["M"], d["N"], d["K"], 0, d["y"].data_ptr(), sh)
-            assert st == 0
-            e2.record(stream)
+        for d in dl:
+            quant(d)
+            gemm(d, d["wq"])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -279,15 +300,26 @@ def run_prefill(args, c: Ctx):
     value = flops_step * args.steps / elapsed / 1e12
     ms_per_step = elapsed / args.steps * 1e3
 
-    q_ms = np.zeros(nl)
-    g_ms = np.zeros(nl)
-    for s in range(args.steps):
-        for li in range(nl):
-            e0, e1, e2 = ev[s][li]
-            q_ms[li] += e0.elapsed_time(e1)
-            g_ms[li] += e1.elapsed_time(e2)
-    q_ms /= args.steps
-    g_ms /= args.steps
+    # Per-kernel durations, enqueued straight after the timed steps so that the chip is as warm
+    # as in them: each layer's quantize, then its GEMM, launched back to back with one event at
+    # each pass boundary (an event between two launches costs a gap and a cache flush). The
+    # GEMMs rotate over copies of the weights (>600 MB per layer) so that each launch, as in
+    # the step, reads them from HBM rather than from the 256 MB last-level cache.
+    reps = max(args.steps, 10)
+    marks = [c.event() for _ in range(2 * nl + 1)]
+    marks[0].record(stream)
+    for li, d in enumerate(dl):
+        for _ in range(reps):
+            quant(d)
+        marks[2 * li + 1].record(stream)
+        for i in range(len(copies[li])):
+            gemm(d, copies[li][i])
+        marks[2 * li + 2].record(stream)
+    torch.cuda.synchronize()
+    q_ms = np.array([marks[2 * li].elapsed_time(marks[2 * li + 1]) / reps for li in range(nl)])
+    g_ms = np.array([marks[2 * li + 1].elapsed_time(marks[2 * li + 2]) / len(copies[li])
+                     for li in range(nl)])
+    del copies
 
     # dominant kernel: the FP8 GEMM (algorithmic 2MNK per launch over its mean duration)
     gemm_flops = np.array([2.0 * d["M"] * d["N"] * d["K"] for d in dl])
@@ -482,27 +514,19 @@ def run_decode(args, c: Ctx):
                 sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
 
-                def launch(i, e=None):
-                    if e:
-                        e[0].record(stream)
+                def quant(i):
                     c.check(L.w8a8_quantize_per_token(x.data_ptr(), M, K, fmt, xq.data_ptr(), sx.data_ptr(), sh))
-                    if e:
-                        e[1].record(stream)
+
+                def gemm(i):
                     c.check(L.w8a8_gemm(xq.data_ptr(), sx.data_ptr(), ws[i % copies].data_ptr(),
                                         sw.data_ptr(), M, N, K, fmt, y.data_ptr(), sh))
-                    if e:
-                        e[2].record(stream)
 
                 for i in range(max(args.warmup, 3)):
-                    launch(i)
+                    quant(i)
+                    gemm(i)
                 R = 3 * copies
-                ev = [(c.event(), c.event(), c.event()) for _ in range(R)]
-                torch.cuda.synchronize()
-                for i in range(R):
-                    launch(i, ev[i])
-                torch.cuda.synchronize()
-                q_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
-                g_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+                q_us = _launch_mean_s(c, quant, R) * 1e6
+                g_us = _launch_mean_s(c, gemm, R) * 1e6
                 byt = N * K + M * K + 2 * M * N + 4 * (M + N)
                 flops = 2.0 * M * N * K
                 attain = min(FP8_PEAK_TFLOPS, flops / byt * HBM_PEAK_GBPS / 1e3)   # TFLOP/s
@@ -559,15 +583,7 @@ def run_w4a16(args, c: Ctx):
 
             for i in range(max(args.warmup, 3)):
                 launch(i)
-            R = 3 * copies
-            ev = [(c.event(), c.event()) for _ in range(R)]
-            torch.cuda.synchronize()
-            for i in range(R):
-                ev[i][0].record(stream)
-                launch(i)
-                ev[i][1].record(stream)
-            torch.cuda.synchronize()
-            g_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
+            g_us = _launch_mean_s(c, launch, 3 * copies) * 1e6
             byt = wbytes + 2 * M * K + 2 * M * N
             flops = 2.0 * M * N * K
             cases.append({"M": M, "N": N, "gemm_us": round(g_us, 2), "gemm_GBps": round(byt / g_us / 1e3, 1),
@@ -607,24 +623,21 @@ def run_w4a16(args, c: Ctx):
 
 # ----------------------------------------------------------------------------- block-scaled
 def _timed_pair(args, c: Ctx, first, second):
-    """Warm up, then time `steps` of first() + second() with events around each."""
-    import numpy as np
+    """Warm up, then time `steps` of first() + second() (nothing else on the stream); then
+    each of the two kernels alone, launched back to back. Returns seconds per step and the
+    two kernels' mean durations."""
     for _ in range(args.warmup):
         first()
         second()
-    ev = [(c.event(), c.event(), c.event()) for _ in range(args.steps)]
     c.torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e in ev:
-        e[0].record(c.stream)
+    for _ in range(args.steps):
         first()
-        e[1].record(c.stream)
         second()
-        e[2].record(c.stream)
     c.torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    a = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
-    b = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    a = _launch_mean_s(c, lambda i: first(), args.steps)
+    b = _launch_mean_s(c, lambda i: second(), args.steps)
     return wall, a, b
 
 
