@@ -62,7 +62,7 @@ def _parse_args():
     p.add_argument("--workload", default="prefill",
                    choices=["prefill", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16", "epilogue", "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    p.add_argument("--cpu-rows", type=int, default=256,
+    p.add_argument("--cpu-rows", type=int, default=1024,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (the reference for "

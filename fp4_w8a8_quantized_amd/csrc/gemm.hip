@@ -1,17 +1,14 @@
-// The tiled GEMM for INT8 (SmoothQuant W8A8) and block-scaled FP8 on gfx950 matrix cores,
-// and the GEMM dispatch (few tokens: gemm_skinny.hip; FP8: gemm_pp.hip; MXFP4:
+// The tiled GEMM for INT8 (SmoothQuant W8A8) on gfx950 matrix cores, and the GEMM
+// dispatch (few tokens: gemm_skinny.hip; FP8 and block-scaled FP8: gemm_pp.hip; MXFP4:
 // gemm_mx_pp.hip).
 //
-//   BLOCK  y = bf16( sum_g s_x[m,g] s_w[n/128,g] partial_g )    v_mfma_f32_16x16x128_f8f6f4, one fp32 partial per 128-K group
 //   INT8   y = bf16( fp32(fp32(acc_i32) s_x[m]) s_w[n] )        v_mfma_i32_32x32x32_i8
 //
 // The scales are applied after the low-precision reduction, which the scale-factoring
 // identity diag(s_X)(X_q W_q^T)diag(s_W) allows ("FP8 and FP4 inference, SmoothQuant and
 // activation quantization", Scale granularity; "FP8 and INT8 Inference" §6-9, the GEMM
-// epilogue; "Low-bit LLM Weights and Activations" §3.4). The block-scaled variant
-// promotes each 128-wide K group's fp32 partial into the running fp32 sum ("FP8 and INT8
-// Inference" §5, What DeepSeek did). INT8 uses the 32x32 MFMA shape, which runs at twice
-// the rate of its 16x16 form on gfx950.
+// epilogue; "Low-bit LLM Weights and Activations" §3.4). INT8 uses the 32x32 MFMA shape,
+// which runs at twice the rate of its 16x16 form on gfx950.
 //
 // One 256-thread workgroup (4 waves, 2 x 2) computes a 256 x BN output tile:
 //  - K advances 128 bytes (128 elements) per step. The X
@@ -29,14 +26,10 @@
 //    now-free LDS, and writes whole rows with 16-byte stores.
 //  - Workgroup ids are remapped so that consecutive tiles (which share a W panel) land
 //    on the same XCD and its L2 (ids are dealt round-robin over the 8 XCDs).
-#include <type_traits>
-
 #include "common.h"
 #include "internal.h"
 
 namespace w8a8 {
-
-enum Kind : int { KIND_INT8 = 1, KIND_BLOCK = 2 };
 
 constexpr int kBM = 256;
 constexpr int kThreads = 256;
@@ -64,30 +57,21 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Makes a register value opaque at this point of the instruction stream. Placed right
-// after a step's barrier, it pins the compiler's wait for a scale load to a moment when
-// no direct-to-LDS load is in flight (vmcnt retires in issue order, so a later wait on an
-// earlier scale load would also wait for every DMA issued after it).
-template <class T>
-__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
-
-template <int BN, int KIND, int STAGES, bool OF8>
+template <int BN, int STAGES, bool OF8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
-            const uint8_t* __restrict__ wq, const void* __restrict__ swp, int M, int N,
+gemm_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
+            const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
             int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
-  constexpr bool MF32 = (KIND == KIND_INT8);
-  constexpr int SUB = MF32 ? 32 : 16;         // MFMA output tile edge
+  constexpr int SUB = 32;                     // MFMA output tile edge
   constexpr int SM = 128 / SUB;               // X subtiles per wave (128 rows)
   constexpr int SN = (BN / 2) / SUB;          // W subtiles per wave (BN/2 rows)
   static_assert(SN * SUB * 2 == BN, "tile width must split into whole subtiles");
   constexpr int XT = kBM * 128, WT = BN * 128, STAGE = XT + WT;
   constexpr int XI = kBM / 32, WI = BN / 32;  // 1 KB DMA instructions per wave per step
   constexpr int DMA_PER_STEP = XI + WI;
-  constexpr int FR = MF32 ? 16 : 8;           // fragment registers per subtile
+  constexpr int FR = 16;                      // fragment registers per subtile
   typedef int frag_t __attribute__((ext_vector_type(FR)));
-  typedef typename std::conditional<KIND == KIND_INT8, int, float>::type acc_e;
-  typedef acc_e acc_t __attribute__((ext_vector_type(MF32 ? 16 : 4)));
+  typedef i32x16 acc_t;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[STAGES * STAGE];
 
   const int t = threadIdx.x, lane = t & 63;
@@ -128,14 +112,13 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   };
   auto dma = [&](int ks, int stage) { dma_part(ks, stage, 0, DMA_PER_STEP); };
 
-  // Fragment map. 16x16x128: lane reads row (lane & 15), chunks 2g, 2g+1 (g = lane >> 4).
-  // 32x32: lane reads row (lane & 31), chunks h, h+2, h+4, h+6 (h = lane >> 5); chunk
-  // 2q + h feeds the q-th of the four 32/64-deep MFMAs of the step.
-  const int fr = MF32 ? (lane & 31) : (lane & 15);
-  const int g = MF32 ? (lane >> 5) : (lane >> 4);
+  // Fragment map: lane reads row (lane & 31), chunks h, h+2, h+4, h+6 (h = lane >> 5);
+  // chunk 2q + h feeds the q-th of the four 32-deep MFMAs of the step.
+  const int fr = lane & 31;
+  const int g = lane >> 5;
   int fo[FR / 4];
 #pragma unroll
-  for (int c = 0; c < FR / 4; ++c) fo[c] = tile_off(fr, MF32 ? (2 * c + g) : (2 * g + c));
+  for (int c = 0; c < FR / 4; ++c) fo[c] = tile_off(fr, 2 * c + g);
   const int xrow0 = wm * 128, wrow0 = wn * (BN / 2);
   auto frag = [&](const uint8_t* base) -> frag_t {
     frag_t f;
@@ -153,31 +136,10 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
     for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{};
 
-  // Scale state (block-scaled: fp32 per row group and W block).
-  const int G = ksteps;
-  int srow[SM], swrow[SN];
-#pragma unroll
-  for (int i = 0; i < SM; ++i) srow[i] = min(m0 + xrow0 + SUB * i + fr, M - 1);
-#pragma unroll
-  for (int j = 0; j < SN; ++j) swrow[j] = min(n0 + wrow0 + SUB * j + fr, N - 1);
-  float bsx[SM], bsw[SN];            // block-scaled: scales of the step being computed
-  auto load_scales = [&](int ks, float (&fx)[SM], float (&fw)[SN]) {
-    if constexpr (KIND == KIND_BLOCK) {
-      const float* sx = reinterpret_cast<const float*>(sxp);
-      const float* sw = reinterpret_cast<const float*>(swp);
-#pragma unroll
-      for (int i = 0; i < SM; ++i) fx[i] = sx[(size_t)srow[i] * G + ks];
-#pragma unroll
-      for (int j = 0; j < SN; ++j)
-        fw[j] = sw[(size_t)(min(n0 + wrow0 + SUB * j, N - 1) >> 7) * G + ks];
-    }
-  };
-
   // ---- prologue: stages 0..STAGES-1 in flight, stage 0 published, F(0) in registers
   frag_t xf[SM], wf0[SN], wf1[SN];
 #pragma unroll
   for (int s = 0; s < STAGES; ++s) dma(min(s, ksteps - 1), s);
-  load_scales(0, bsx, bsw);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 1) * DMA_PER_STEP, 15));
   lds_barrier();
 #pragma unroll
@@ -198,45 +160,18 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     // guarantees that stage ks (read during the previous step) is free.
     __builtin_amdgcn_s_waitcnt(waitcnt_imm((STAGES - 2) * DMA_PER_STEP, 0));
     lds_barrier();
-    if constexpr (KIND == KIND_BLOCK) {
-#pragma unroll
-      for (int i = 0; i < SM; ++i) pin(bsx[i]);
-#pragma unroll
-      for (int j = 0; j < SN; ++j) pin(bsw[j]);
-    }
-    float nsx[SM], nsw[SN];
-    load_scales(min(ks + 1, ksteps - 1), nsx, nsw);
     const int kdma = min(ks + STAGES, ksteps - 1);
     const uint8_t* X = lds + ((ks + 1) % STAGES) * STAGE;
     const uint8_t* W = X + XT;
-    // Block-scaled: each MFMA is one 128-wide K group; its fp32 product is promoted into
-    // the running sum (times s_x[m,g] s_w[n/128,g], one factor per lane) PD MFMAs later,
-    // so that the promotion never waits on the MFMA it follows and PD products are in
-    // flight in distinct registers.
-    constexpr int PD = 4;
-    f32x4 pp[PD];
-    auto promote = [&](int t) {
-      if constexpr (KIND == KIND_BLOCK) {
-        const int ti = t / SN, tj = t % SN;
-        acc[tj][ti] += pp[t % PD] * (bsx[ti] * bsw[tj]);
-      }
-    };
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
-        if constexpr (KIND == KIND_BLOCK) {
-          const int t = i * SN + j;
-          if (t >= PD) promote(t - PD);
-          pp[t % PD] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wcur[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);      // keep the promotion PD MFMAs behind
-        } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const i32x4 a = {wcur[j][4 * q], wcur[j][4 * q + 1], wcur[j][4 * q + 2], wcur[j][4 * q + 3]};
-            const i32x4 bb = {xf[i][4 * q], xf[i][4 * q + 1], xf[i][4 * q + 2], xf[i][4 * q + 3]};
-            acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bb, acc[j][i], 0, 0, 0);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const i32x4 a = {wcur[j][4 * q], wcur[j][4 * q + 1], wcur[j][4 * q + 2], wcur[j][4 * q + 3]};
+          const i32x4 bb = {xf[i][4 * q], xf[i][4 * q + 1], xf[i][4 * q + 2], xf[i][4 * q + 3]};
+          acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, bb, acc[j][i], 0, 0, 0);
         }
       }
       xf[i] = frag(X + (xrow0 + SUB * i) * 128);
@@ -245,14 +180,6 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     }
 #pragma unroll
     for (int j = SM; j < SN; ++j) wnxt[j] = frag(W + (wrow0 + SUB * j) * 128);
-    if constexpr (KIND == KIND_BLOCK) {
-#pragma unroll
-      for (int t = SM * SN - PD; t < SM * SN; ++t) promote(t);
-    }
-#pragma unroll
-    for (int i = 0; i < SM; ++i) bsx[i] = nsx[i];
-#pragma unroll
-    for (int j = 0; j < SN; ++j) bsw[j] = nsw[j];
   };
   int ks = 0;
   for (; ks + 1 < ksteps; ks += 2) {
@@ -275,8 +202,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   };
   // The per-row and per-column scales (and biases) this lane needs are loaded in one
   // batch, so their latencies overlap, before the first epilogue barrier.
-  constexpr int NG = MF32 ? 4 : 1;            // runs of 4 columns per lane per subtile
-  constexpr bool SCALED = (KIND == KIND_INT8);
+  constexpr int NG = 4;                       // runs of 4 columns per lane per subtile
   float esm[SM], esn[SN][NG][4], ebias[SN][NG][4];
   const bool has_bias = ep.bias != nullptr;
 #pragma unroll
@@ -285,22 +211,17 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     for (int q = 0; q < NG; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int n = min(n0 + wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g) + r, N - 1);
-        if constexpr (SCALED) esn[j][q][r] = reinterpret_cast<const float*>(swp)[n];
+        const int n = min(n0 + wrow0 + SUB * j + 8 * q + 4 * g + r, N - 1);
+        esn[j][q][r] = sw[n];
         ebias[j][q][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
       }
-  if constexpr (SCALED) {
 #pragma unroll
-    for (int i = 0; i < SM; ++i) esm[i] = reinterpret_cast<const float*>(sxp)[min(m0 + xrow0 + SUB * i + fr, M - 1)];
-  }
+  for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + SUB * i + fr, M - 1)];
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
   lds_barrier();
-  // FP8 and INT8 tiles check bias and activation at run time (ACT = -1; one copy of the
-  // element loop keeps the widest INT8 tile within its registers); the block-scaled and
-  // MXFP4 GEMMs have no epilogue options, so their loop is compiled without the checks.
-  auto stage = [&](auto act_c, auto bias_c) {
-    constexpr int ACT = decltype(act_c)::value;
-    constexpr bool BIAS = decltype(bias_c)::value;
+  // Bias and activation are checked at run time: one copy of the element loop keeps the
+  // widest tile within its registers.
+  {
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
       const int rl = xrow0 + SUB * i + fr;
@@ -308,29 +229,18 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
       for (int j = 0; j < SN; ++j) {
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
-          const int cl = wrow0 + SUB * j + (MF32 ? 8 * q + 4 * g : 4 * g);
+          const int cl = wrow0 + SUB * j + 8 * q + 4 * g;
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const acc_e a = acc[j][i][4 * q + r];
-            if constexpr (KIND == KIND_INT8) {
-              v[r] = mul_rn(mul_rn((float)a, esm[i]), esn[j][q][r]);
-            } else {
-              v[r] = a;
-            }
-            if constexpr (ACT < 0) {
-              if (has_bias) v[r] = add_rn(v[r], ebias[j][q][r]);
-              v[r] = epi_activate(v[r], ep.act);
-            } else {
-              if constexpr (BIAS) v[r] = add_rn(v[r], ebias[j][q][r]);
-              v[r] = epi_act<ACT>(v[r]);
-            }
+            v[r] = mul_rn(mul_rn((float)acc[j][i][4 * q + r], esm[i]), esn[j][q][r]);
+            if (has_bias) v[r] = add_rn(v[r], ebias[j][q][r]);
+            v[r] = epi_activate(v[r], ep.act);
           }
           if constexpr (OF8) {
-            constexpr bool EX = (KIND == KIND_INT8);
             *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
-                pack_e4m3x4(epi_requant<EX>(v[0], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[1], ep.s_out, ep.inv_s_out),
-                            epi_requant<EX>(v[2], ep.s_out, ep.inv_s_out), epi_requant<EX>(v[3], ep.s_out, ep.inv_s_out));
+                pack_e4m3x4(epi_requant<true>(v[0], ep.s_out, ep.inv_s_out), epi_requant<true>(v[1], ep.s_out, ep.inv_s_out),
+                            epi_requant<true>(v[2], ep.s_out, ep.inv_s_out), epi_requant<true>(v[3], ep.s_out, ep.inv_s_out));
           } else {
             const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
             *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
@@ -338,9 +248,7 @@ gemm_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
         }
       }
     }
-  };
-  if constexpr (SCALED) stage(std::integral_constant<int, -1>{}, std::false_type{});
-  else stage(std::integral_constant<int, 0>{}, std::false_type{});
+  }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   lds_barrier();
   constexpr int EPC = 16 / ES;                 // output elements per 16-byte chunk
@@ -380,34 +288,31 @@ static int pick_bn(int64_t M, int64_t N, const int* cands, int nc) {
   return best;
 }
 
-template <int BN, int KIND, int STAGES, bool OF8 = false>
-static hipError_t launch_bn(hipStream_t st, const void* xq, const void* sx, const void* wq,
-                            const void* sw, int64_t M, int64_t N, int64_t Kb, void* y,
+template <int BN, int STAGES, bool OF8>
+static hipError_t launch_bn(hipStream_t st, const void* xq, const float* sx, const void* wq,
+                            const float* sw, int64_t M, int64_t N, int64_t Kb, void* y,
                             const Epilogue& ep = Epilogue{}) {
   const int tiles_m = (int)((M + kBM - 1) / kBM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int ksteps = (int)(Kb / 128);
   // 16-byte row stores need 16-byte aligned rows: N % 8 == 0 for bf16, N % 16 for bytes.
   const int vec = OF8 ? (N % 16) == 0 : (N % 8) == 0;
-  hipLaunchKernelGGL((gemm_kernel<BN, KIND, STAGES, OF8>), dim3((unsigned)(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((gemm_kernel<BN, STAGES, OF8>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(kThreads), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
                      (int)M, (int)N, (int)Kb, ksteps, y, tiles_m, vec, ep);
   return hipGetLastError();
 }
 
-// Tile widths per variant. The 32x32 INT8 variant needs multiples of 64. The
-// block-scaled variant keeps a per-group partial and its scales in registers, so it
-// stops at 192; the scale-carrying variants use two stages so that one vmcnt(0) per step
-// also retires their scale loads.
+// Tile widths: the 32x32 MFMA tiles need multiples of 64.
 template <bool OF8>
 static hipError_t launch_int8(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                               const Epilogue& ep) {
   static const int c[3] = {256, 192, 128};
   switch (pick_bn(M, N, c, 3)) {
-    case 256: return launch_bn<256, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-    case 192: return launch_bn<192, KIND_INT8, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
-    default: return launch_bn<128, KIND_INT8, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    case 256: return launch_bn<256, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    case 192: return launch_bn<192, 2, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
+    default: return launch_bn<128, 3, OF8>(st, xq, sx, wq, sw, M, N, K, y, ep);
   }
 }
 
@@ -420,16 +325,6 @@ hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const fl
   if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
   if (ep.out_fp8) return launch_int8<true>(xq, sx, wq, sw, M, N, K, y, st, ep);
   return launch_int8<false>(xq, sx, wq, sw, M, N, K, y, st, ep);
-}
-
-hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
-                                   const float* sw, int64_t M, int64_t N, int64_t K, void* y,
-                                   hipStream_t st) {
-  static const int c[2] = {192, 128};
-  switch (pick_bn(M, N, c, 2)) {
-    case 192: return launch_bn<192, KIND_BLOCK, 2>(st, xq, sx, wq, sw, M, N, K, y);
-    default: return launch_bn<128, KIND_BLOCK, 2>(st, xq, sx, wq, sw, M, N, K, y);
-  }
 }
 
 }  // namespace w8a8

@@ -31,6 +31,19 @@
 //
 // Epilogue: scale, bias, activation, convert (bf16, or E4M3FN of clamp(v / s_out)) in
 // registers, stage the tile through the freed LDS, write whole rows with 16-byte stores.
+//
+// Block-scaled form (BLK; the DeepSeek-V3 recipe of "FP8 and INT8 Inference" §5: 1 x 128
+// activation groups, 128 x 128 weight blocks, FP32 accumulation promoted at intervals):
+//   y = bf16( sum_g s_x[m,g] s_w[n/128,g] sum_{k in g} dec(xq[m,k]) dec(wq[n,k]) )
+// A K step is one 128-wide group, and each 16 x 16 subtile takes exactly one MFMA per step,
+// so the MFMA (with a zero accumulator) yields the group's fp32 partial, which is promoted
+// into the running sum with one FMA per element, times s_x[m,g] s_w[n/128,g]. The
+// promotion of a subtile runs four MFMAs behind its product (the last four of a step
+// during the next LDS phase), so it never waits on the matrix core. Group A, which issues
+// no direct-to-LDS loads and may therefore use ordinary loads, fetches the 256 rows' s_x
+// and the tile's s_w two steps ahead and publishes their products to a double-buffered
+// 1 KB LDS area, laid out so that each lane reads its four rows with one 16-byte read.
+// Tiles are 128 wide, one weight block, so every column of a tile shares s_w.
 #include "common.h"
 #include "internal.h"
 
@@ -59,12 +72,13 @@ constexpr int pp_wait(int vm, int lgkm) {
 
 __device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BN, bool OF8>
+template <int BN, bool OF8, bool BLK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
                int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
   constexpr int BM = kPPBM;
+  static_assert(!BLK || (BN == 128 && !OF8), "block scales: 128-wide tiles (one weight block), bf16 out");
   // Wave tiles: 128 x BN/4 (2 x 4 waves), or 64 x 64 at BN = 128 (4 x 2 waves), which reads
   // 8 fragments per step instead of 10 for the same 64 accumulators.
   constexpr int WAVES_M = (BN == 128) ? 4 : 2;
@@ -78,6 +92,10 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   constexpr int DMA = XI + WI;
   constexpr int DC = DMA / 2;                 // of which issued during the MFMA phase
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  // Block scales s_x[m,g] s_w[n/128,g] of two steps (buffer g & 1): row r of the tile sits at
+  // (r & ~63) + 4 (r & 15) + ((r >> 4) & 3), so lane l of a wave reads rows 16 i + (l & 15)
+  // of its 64-row wave tile (i = 0..3) as one float4.
+  __shared__ __attribute__((aligned(16))) float sxl[BLK ? 2 * BM : 4];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -123,6 +141,26 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     for (int i = 0; i < SM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   frag_t xf[SM], wf[SN];
 
+  constexpr int T = SM * SN;
+  // Block-scaled state: the last PD group partials (ring indexed by subtile number) and the
+  // scales of the step they belong to. Zero at the start, so that the first step's
+  // promotion of "the previous step's tail" adds 0 * 0.
+  constexpr int PD = 4;
+  f32x4 pp[BLK ? PD : 1];
+  float bscl[BLK ? SM : 1];
+  if constexpr (BLK) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) pp[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < SM; ++i) bscl[i] = 0.f;
+  }
+  auto promote = [&](int tt) {                         // subtile tt's partial into its sum
+    if constexpr (BLK) {
+      const int ti = tt / SN, tj = tt % SN;
+      acc[tj][ti] += pp[tt % PD] * bscl[ti];
+    }
+  };
+
   auto lds_phase = [&](int ks) {
     const uint8_t* X = lds + (ks & 1) * STAGE;
     const uint8_t* W = X + XT;
@@ -130,47 +168,88 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     for (int i = 0; i < SM; ++i) xf[i] = frag(X + (xrow0 + 16 * i) * 128);
 #pragma unroll
     for (int j = 0; j < SN; ++j) wf[j] = frag(W + (wrow0 + 16 * j) * 128);
-    __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));      // this wave's reads of the stage done
+    if constexpr (BLK) {
+      const f32x4 s4 = *reinterpret_cast<const f32x4*>(sxl + (ks & 1) * BM + xrow0 + 4 * fr);
+      // The previous step's last PD promotions, while the reads are in flight.
+#pragma unroll
+      for (int tt = T - PD; tt < T; ++tt) promote(tt);
+      __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));
+#pragma unroll
+      for (int i = 0; i < SM; ++i) bscl[i] = s4[i];
+    } else {
+      __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));    // this wave's reads of the stage done
+    }
   };
-  constexpr int T = SM * SN;
-  // MFMAs number lo .. hi-1 of a step (row-major over the SM x SN subtiles).
+  // MFMA number tt of a step (row-major over the SM x SN subtiles). Block-scaled: the
+  // product goes to the partial ring, after the promotion of the partial PD MFMAs back,
+  // which held the same ring slot.
+  auto mfma_one = [&](int tt) {
+    const int i = tt / SN, j = tt % SN;
+    if constexpr (BLK) {
+      if (tt >= PD) promote(tt - PD);
+      pp[tt % PD] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    } else {
+      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  // MFMAs number lo .. hi-1 of a step.
   auto mfma_range = [&](int lo, int hi) {
 #pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-      for (int j = 0; j < SN; ++j)
-        if (i * SN + j >= lo && i * SN + j < hi)
-          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+    for (int tt = lo; tt < hi; ++tt) {
+      mfma_one(tt);
+      if constexpr (BLK) __builtin_amdgcn_sched_barrier(0);
+    }
   };
   // Group B's MFMA phase, with the last DC loads of step kd between the MFMAs.
   auto mfma_phase_loading = [&](int kd, int stage) {
 #pragma unroll
-    for (int i = 0; i < SM; ++i)
+    for (int tt = 0; tt < T; ++tt) {
+      mfma_one(tt);
 #pragma unroll
-      for (int j = 0; j < SN; ++j) {
-        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
-        const int tt = i * SN + j;
-#pragma unroll
-        for (int d = 0; d < DC; ++d)
-          if (tt == (d * T) / DC) dma_one(kd, stage, DMA - DC + d);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int d = 0; d < DC; ++d)
+        if (tt == (d * T) / DC) dma_one(kd, stage, DMA - DC + d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Block scales: group A thread t (< 256) fetches row m0 + t's s_x and the tile's s_w two
+  // steps ahead and publishes their product for the next step (ks + 1) during step ks.
+  const int srow = min(m0 + (t & (BM - 1)), M - 1);
+  const int spos = (t & (BM - 1) & ~63) + 4 * (t & 15) + ((t >> 4) & 3);
+  const float* sxr = sx + (size_t)srow * ksteps;
+  const float* swr = sw + (size_t)tn * ksteps;
+  float sx_next = 0.f, sw_next = 0.f;
+  auto publish = [&](int ks) {                         // group A: scales of step ks + 1
+    if constexpr (BLK) {
+      sxl[((ks + 1) & 1) * BM + spos] = sx_next * sw_next;
+      const int k2 = min(ks + 2, ksteps - 1);
+      sx_next = sxr[k2];
+      sw_next = swr[k2];
+    }
   };
 
   // The epilogue's scales (and biases) are loaded up front; their latency hides behind
   // the K loop.
   float esm[SM], esn[SN][4], ebias[SN][4];
-  const bool has_bias = ep.bias != nullptr;
+  const bool has_bias = !BLK && ep.bias != nullptr;
+  if constexpr (!BLK) {
 #pragma unroll
-  for (int j = 0; j < SN; ++j)
+    for (int j = 0; j < SN; ++j)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1);
-      esn[j][r] = sw[n];
-      ebias[j][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int n = min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1);
+        esn[j][r] = sw[n];
+        ebias[j][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
+      }
 #pragma unroll
-  for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + 16 * i + fr, M - 1)];
+    for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + 16 * i + fr, M - 1)];
+  } else if (grp == 0) {
+    // Scales of step 0 published before the first barrier; step 1's in registers.
+    sxl[spos] = sxr[0] * swr[0];
+    sx_next = sxr[min(1, ksteps - 1)];
+    sw_next = swr[min(1, ksteps - 1)];
+    __builtin_amdgcn_s_waitcnt(pp_wait(63, 0));
+  }
   // Prologue: group B loads steps 0 and 1; step 0 landed and published. Past the last
   // step, loads re-fetch the last step into a stage nobody reads again (branch-free).
   if (grp == 1) {
@@ -184,6 +263,7 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   // Both groups pass 3 * ksteps + 1 barriers in the loop part.
   if (grp == 0) {
     for (int ks = 0; ks < ksteps; ++ks) {
+      publish(ks);
       lds_phase(ks);                                   // slot 2k
       __builtin_amdgcn_sched_barrier(0);
       pp_barrier();
@@ -224,6 +304,11 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     for (; ks < ksteps; ++ks) iter(ks, std::false_type{});
   }
 
+  if constexpr (BLK) {
+#pragma unroll
+    for (int tt = T - PD; tt < T; ++tt) promote(tt);   // the last step's tail
+  }
+
   // ---- epilogue. Every load has landed and every wave is past its last fragment read.
   constexpr int ES = OF8 ? 1 : 2;                      // output bytes per element
   constexpr bool SWZ = (BN == 256 && !OF8);
@@ -248,7 +333,7 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = acc[j][i][r] * (esm[i] * esn[j][r]);
+          v[r] = BLK ? acc[j][i][r] : acc[j][i][r] * (esm[i] * esn[j][r]);
           if constexpr (BIAS) v[r] = add_rn(v[r], ebias[j][r]);
           v[r] = epi_act<ACT>(v[r]);
         }
@@ -299,13 +384,13 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   }
 }
 
-template <int BN, bool OF8>
+template <int BN, bool OF8, bool BLK = false>
 hipError_t launch_pp(const void* xq, const float* sx, const void* wq, const float* sw, int64_t M,
                      int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
   const int tiles_m = (int)((M + kPPBM - 1) / kPPBM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int vec = OF8 ? (N % 16) == 0 : (N % 8) == 0;
-  hipLaunchKernelGGL((gemm_pp_kernel<BN, OF8>), dim3((unsigned)(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((gemm_pp_kernel<BN, OF8, BLK>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(kPPThreads), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
                      (int)M, (int)N, (int)K, (int)(K / 128), y, tiles_m, vec, ep);
   return hipGetLastError();
@@ -328,6 +413,13 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                 : launch_pp<128, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
   return wide ? launch_pp<192, false>(xq, sx, wq, sw, M, N, K, y, st, ep)
               : launch_pp<128, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+}
+
+// Block-scaled FP8 (s_x [M, K/128], s_w [ceil(N/128), K/128]): 256 x 128 tiles, bf16 out.
+hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
+                                   const float* sw, int64_t M, int64_t N, int64_t K, void* y,
+                                   hipStream_t st) {
+  return launch_pp<128, false, true>(xq, sx, wq, sw, M, N, K, y, st, Epilogue{});
 }
 
 }  // namespace w8a8

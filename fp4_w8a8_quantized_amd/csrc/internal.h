@@ -48,6 +48,8 @@ inline bool use_skinny(int64_t M, int64_t N) { return M <= 64 || (M <= 128 && N 
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                               const Epilogue& ep);
+// Block-scaled FP8 on the two-waves-per-SIMD kernel (256 x 128 tiles, one weight block
+// wide; each 128-K group's partial promoted with its scales).
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                    hipStream_t st);

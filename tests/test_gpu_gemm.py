@@ -248,6 +248,42 @@ def test_blockscaled_ragged(M, N, K):
     _block_compare(xb, wb, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(513, 384, 2048), (256, 130, 1280)])
+def test_blockscaled_scales_span_binades(M, N, K):
+    """Every 1 x 128 activation group, token and 128 x 128 weight block at its own power of
+    two (2^-12 .. 2^12): applying a neighbouring group's, row's or block's scale in the
+    promotion moves the output by orders of magnitude."""
+    need_gpu()
+    rng = np.random.default_rng(M + 7 * N + K)
+    G_ = K // 128
+    xs = np.exp2(rng.integers(-12, 13, size=(M, G_))).repeat(128, axis=1)
+    ws = np.exp2(rng.integers(-12, 13, size=((N + 127) // 128, G_))).repeat(128, axis=0)
+    ws = ws.repeat(128, axis=1)[:N]
+    xb = _bf16(rng.standard_normal((M, K)) * xs)
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02 * ws)
+    _block_compare(xb, wb, f"binade-scaled {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 1024, 1024), (1024, 2048, 4096)])
+def test_blockscaled_repeat_identical(M, N, K):
+    """The block-scaled GEMM shares the FP8 kernel's stage refills and adds its own
+    double-buffered scale area in LDS: repeated launches must give identical bits."""
+    need_gpu()
+    rng = np.random.default_rng(M + N + K + 1)
+    xb = _bf16(rng.standard_t(3, size=(M, K)))
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02)
+    xq, sx = w8.quantize_per_token_group(to_dev_bf16(xb))
+    wq, sw = w8.quantize_weight_block(to_dev_bf16(wb))
+    y0 = w8.gemm_blockscaled(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    ref = y0.clone()
+    for r in range(12):
+        w8.gemm_blockscaled(xq, sx, wq, sw, out=y0)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), ref.view(torch.int16)), f"{M}x{N}x{K}: run {r + 1} differs"
+    _block_compare(xb, wb, f"repeat {M}x{N}x{K}")
+
+
 def test_blockscaled_full_size_sampled():
     need_gpu()
     xb, wb = synthetic.blockscaled()
