@@ -62,7 +62,7 @@ def _parse_args():
     p.add_argument("--workload", default="prefill",
                    choices=["prefill", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16", "epilogue", "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    p.add_argument("--cpu-rows", type=int, default=1024,
+    p.add_argument("--cpu-rows", type=int, default=2048,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (the reference for "
@@ -266,8 +266,9 @@ def run_prefill(args, c: Ctx):
         dl.append(dict(name=name, x=x, xq=xq, sx=sx, wq=wq, sw=sw, y=y, M=M, N=N, K=K))
     torch.cuda.synchronize()
 
-    def quant(d):
-        c.check(L.w8a8_quantize_per_token(d["x"].data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
+    def quant(d, x=None):
+        x = d["x"] if x is None else x
+        c.check(L.w8a8_quantize_per_token(x.data_ptr(), d["M"], d["K"], 0, d["xq"].data_ptr(),
                                           d["sx"].data_ptr(), sh))
 
     def gemm(d, wq):
@@ -300,26 +301,48 @@ def run_prefill(args, c: Ctx):
     value = flops_step * args.steps / elapsed / 1e12
     ms_per_step = elapsed / args.steps * 1e3
 
-    # Per-kernel durations, enqueued straight after the timed steps so that the chip is as warm
-    # as in them: each layer's quantize, then its GEMM, launched back to back with one event at
-    # each pass boundary (an event between two launches costs a gap and a cache flush). The
-    # GEMMs rotate over copies of the weights (>600 MB per layer) so that each launch, as in
-    # the step, reads them from HBM rather than from the 256 MB last-level cache.
+    # Per-kernel durations. Each pass launches one kernel back to back between two HIP events
+    # (an event between two launches costs a gap and a cache flush). Two untimed steps go
+    # first, so that the chip is as warm as in the timed steps and the host has queued the
+    # whole pass before the GPU reaches it (short kernels would otherwise wait on launches).
+    # The GEMMs rotate over copies of the weights and the quantizer over copies of X (each
+    # >600 MB per layer), so that every launch reads its operands from HBM as in the step,
+    # where the weight stream pushes X out of the 256 MB last-level cache. A third pass
+    # repeats the quantizer on one X, which then stays in that cache, and a fourth times a
+    # plain device copy of the quantizer's bytes (1.5 B read and 1.5 B written per element of
+    # X, against its 2 + 1) over rotating buffers: what HBM gives at these sizes.
+    def spacer():
+        for _ in range(2):
+            for d in dl:
+                quant(d)
+                gemm(d, d["wq"])
+
+    def timed_pass(fn, n):
+        e0, e1 = c.event(), c.event()
+        torch.cuda.synchronize()
+        spacer()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n                  # ms per launch
+
     reps = max(args.steps, 10)
-    marks = [c.event() for _ in range(2 * nl + 1)]
-    marks[0].record(stream)
+    g_ms, q_ms, qc_ms, cp_ms = [], [], [], []
     for li, d in enumerate(dl):
-        for _ in range(reps):
-            quant(d)
-        marks[2 * li + 1].record(stream)
-        for i in range(len(copies[li])):
-            gemm(d, copies[li][i])
-        marks[2 * li + 2].record(stream)
-    torch.cuda.synchronize()
-    q_ms = np.array([marks[2 * li].elapsed_time(marks[2 * li + 1]) / reps for li in range(nl)])
-    g_ms = np.array([marks[2 * li + 1].elapsed_time(marks[2 * li + 2]) / len(copies[li])
-                     for li in range(nl)])
+        g_ms.append(timed_pass(lambda i, d=d, w=copies[li]: gemm(d, w[i]), len(copies[li])))
+        xc = [d["x"]] + [d["x"].clone() for _ in range(max(reps, math.ceil(600e6 / d["x"].nbytes)) - 1)]
+        q_ms.append(timed_pass(lambda i, d=d, xc=xc: quant(d, xc[i]), len(xc)))
+        del xc
+        qc_ms.append(timed_pass(lambda i, d=d: quant(d), reps))
+        nb = (3 * d["M"] * d["K"]) // 2
+        bufs = [torch.empty((nb,), dtype=torch.uint8, device=c.dev)
+                for _ in range(2 * max(10, math.ceil(600e6 / nb)))]
+        cp_ms.append(timed_pass(lambda i, b=bufs: b[2 * i + 1].copy_(b[2 * i]), len(bufs) // 2))
+        del bufs
     del copies
+    g_ms, q_ms, qc_ms, cp_ms = map(np.array, (g_ms, q_ms, qc_ms, cp_ms))
 
     # dominant kernel: the FP8 GEMM (algorithmic 2MNK per launch over its mean duration)
     gemm_flops = np.array([2.0 * d["M"] * d["N"] * d["K"] for d in dl])
@@ -328,12 +351,16 @@ def run_prefill(args, c: Ctx):
     # quantize kernel: 2 B read + 1 B written per element + 4 B per row scale
     q_bytes = np.array([3.0 * d["M"] * d["K"] + 4.0 * d["M"] for d in dl])
     q_gbps = float(q_bytes.mean() / (q_ms.mean() * 1e-3) / 1e9)
+    qc_gbps = float(q_bytes.mean() / (qc_ms.mean() * 1e-3) / 1e9)
+    cp_gbps = float(q_bytes.mean() / (cp_ms.mean() * 1e-3) / 1e9)
 
     per_layer = {d["name"]: {"M": d["M"], "N": d["N"], "K": d["K"],
                              "gemm_us": round(g_ms[i] * 1e3, 2),
                              "gemm_tflops": round(gemm_flops[i] / (g_ms[i] * 1e-3) / 1e12, 1),
                              "quant_us": round(q_ms[i] * 1e3, 2),
-                             "quant_GBps": round(q_bytes[i] / (q_ms[i] * 1e-3) / 1e9, 1)}
+                             "quant_GBps": round(q_bytes[i] / (q_ms[i] * 1e-3) / 1e9, 1),
+                             "quant_cached_us": round(qc_ms[i] * 1e3, 2),
+                             "copy_same_bytes_us": round(cp_ms[i] * 1e3, 2)}
                  for i, d in enumerate(dl)}
 
     rec = _base_record(
@@ -351,6 +378,9 @@ def run_prefill(args, c: Ctx):
                       "quantize_fp8_mean_us": round(float(q_ms.mean()) * 1e3, 2),
                       "quantize_fp8_GBps": round(q_gbps, 1),
                       "quantize_fp8_hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+                      "quantize_fp8_cached_GBps": round(qc_gbps, 1),
+                      "copy_same_bytes_GBps": round(cp_gbps, 1),
+                      "quantize_over_copy": round(q_gbps / cp_gbps, 4),
                       "per_layer": per_layer,
                       "gemm_source_sha256_16": gemm_source_hash()}
     if not args.no_cpu_baseline:
