@@ -6,8 +6,9 @@
 // Why two waves per SIMD. A wave issues in order: with one wave per SIMD, every LDS read
 // and every direct-to-LDS load it issues sits between two MFMAs, and the CU's address
 // unit (about 64 B per clock) and LDS latency hold back the matrix core. Here a 512-thread
-// workgroup (8 waves, 2 per SIMD) computes a 256 x BN tile; each wave owns 128 x BN/4 of
-// it (64 x 64 at BN = 128). Waves 0-3 (group A) and 4-7 (group B) alternate between two
+// workgroup (8 waves, 2 per SIMD) computes a 256 x BN tile, BN in {128, 192, 224}; each
+// wave owns 128 x 48 of it at BN = 192, else 64 x BN/2. Waves 0-3 (group A) and 4-7
+// (group B) alternate between two
 // phases separated by workgroup barriers:
 //   LDS phase:  read this step's X and W fragments into registers
 //   MFMA phase: SM x SN MFMAs on them
@@ -79,9 +80,10 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
   constexpr int BM = kPPBM;
   static_assert(!BLK || (BN == 128 && !OF8), "block scales: 128-wide tiles (one weight block), bf16 out");
-  // Wave tiles: 128 x BN/4 (2 x 4 waves), or 64 x 64 at BN = 128 (4 x 2 waves), which reads
-  // 8 fragments per step instead of 10 for the same 64 accumulators.
-  constexpr int WAVES_M = (BN == 128) ? 4 : 2;
+  // Wave tiles: 128 x 48 at BN = 192 (2 x 4 waves); 64 x BN/2 otherwise (4 x 2 waves): at
+  // BN = 128 that reads 8 fragments per step instead of 10 for the same 64 accumulators, and
+  // at BN = 224 (64 x 112) 11 fragments for 28 MFMAs.
+  constexpr int WAVES_M = (BN == 192) ? 2 : 4;
   constexpr int WR = BM / WAVES_M;            // rows per wave
   constexpr int SM = WR / 16;                 // 16-row subtiles
   constexpr int WC = BN * WAVES_M / 8;        // columns per wave
@@ -228,19 +230,20 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     }
   };
 
-  // The epilogue's scales (and biases) are loaded up front; their latency hides behind
-  // the K loop.
-  float esm[SM], esn[SN][4], ebias[SN][4];
+  // The epilogue's scales are loaded up front, so that their latency hides behind the K
+  // loop, except the column scales of the 224-wide tile, whose registers it cannot spare
+  // during the loop (the bias is read in the epilogue).
+  constexpr bool LATE_SN = (BN == 224);
+  float esm[SM], esn[SN][4];
   const bool has_bias = !BLK && ep.bias != nullptr;
-  if constexpr (!BLK) {
+  auto load_esn = [&]() {
 #pragma unroll
     for (int j = 0; j < SN; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1);
-        esn[j][r] = sw[n];
-        ebias[j][r] = has_bias ? bf16_lo(ep.bias[n]) : 0.f;
-      }
+      for (int r = 0; r < 4; ++r) esn[j][r] = sw[min(n0 + wrow0 + 16 * j + 4 * g + r, N - 1)];
+  };
+  if constexpr (!BLK) {
+    if constexpr (!LATE_SN) load_esn();
 #pragma unroll
     for (int i = 0; i < SM; ++i) esm[i] = sx[min(m0 + xrow0 + 16 * i + fr, M - 1)];
   } else if (grp == 0) {
@@ -308,6 +311,7 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 #pragma unroll
     for (int tt = T - PD; tt < T; ++tt) promote(tt);   // the last step's tail
   }
+  if constexpr (!BLK && LATE_SN) load_esn();
 
   // ---- epilogue. Every load has landed and every wave is past its last fragment read.
   constexpr int ES = OF8 ? 1 : 2;                      // output bytes per element
@@ -334,7 +338,7 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           v[r] = BLK ? acc[j][i][r] : acc[j][i][r] * (esm[i] * esn[j][r]);
-          if constexpr (BIAS) v[r] = add_rn(v[r], ebias[j][r]);
+          if constexpr (BIAS) v[r] = add_rn(v[r], bf16_lo(ep.bias[min(n0 + cl + r, N - 1)]));
           v[r] = epi_act<ACT>(v[r]);
         }
         if constexpr (OF8) {
@@ -399,20 +403,25 @@ hipError_t launch_pp(const void* xq, const float* sx, const void* wq, const floa
 }  // namespace
 
 // Tile width: the one whose waves of workgroups over the 256 CUs cost least, weighting
-// each width by its measured steady-state MFMA efficiency (0.80 at 192, 0.66 at 128 on
-// MI355X: the wider tile spends a smaller share of each step on loads and barriers).
+// each width by its measured steady-state MFMA efficiency (0.83 at 224, 0.80 at 192, 0.66
+// at 128 on MI355X: a wider tile spends a smaller share of each step on loads, fragment
+// reads and barriers). 224 wins where it removes a partial wave, as for 2048 x 28672
+// (1024 tiles, four full waves, against 1200 tiles of 192).
 hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const float* sw,
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep) {
   const int64_t tm = (M + kPPBM - 1) / kPPBM;
-  const int64_t waves192 = (tm * ((N + 191) / 192) + 255) / 256;
-  const int64_t waves128 = (tm * ((N + 127) / 128) + 255) / 256;
-  const bool wide = waves192 * 240 <= waves128 * 194;   // 192 / 0.80 vs 128 / 0.66
-  if (ep.out_fp8)
-    return wide ? launch_pp<192, true>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                : launch_pp<128, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  return wide ? launch_pp<192, false>(xq, sx, wq, sw, M, N, K, y, st, ep)
-              : launch_pp<128, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  auto cost = [&](int64_t bn, int64_t per_tile) { return ((tm * ((N + bn - 1) / bn) + 255) / 256) * per_tile; };
+  const int64_t c224 = cost(224, 270), c192 = cost(192, 240), c128 = cost(128, 194);
+  const int bn = (c224 < c192 && c224 < c128) ? 224 : (c192 <= c128 ? 192 : 128);
+  if (ep.out_fp8) {
+    if (bn == 224) return launch_pp<224, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    return bn == 192 ? launch_pp<192, true>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                     : launch_pp<128, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  }
+  if (bn == 224) return launch_pp<224, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return bn == 192 ? launch_pp<192, false>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                   : launch_pp<128, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 // Block-scaled FP8 (s_x [M, K/128], s_w [ceil(N/128), K/128]): 256 x 128 tiles, bf16 out.

@@ -123,6 +123,38 @@ def test_fp8_requantized_out(M, N, K, fmt):
                 _check_fp8_codes(codes, z, what)
 
 
+# The 224-wide tile, which the dispatcher picks for 2048-token layers of about 28672
+# outputs (gate+up): ragged rows and columns, the plain GEMM, bias with SiLU, and FP8
+# outputs, compared on sampled rows that include the first, last and tile-edge rows.
+WIDE_SHAPES = [(1999, 28001, 256), (2048, 28016, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
+def test_wide_tile_sampled(M, N, K):
+    need_gpu()
+    dev, ora = _setup("e4m3fn", M, N, K, M + N + K)
+    rng = np.random.default_rng(M * N)
+    rows = np.unique(np.r_[0, 1, 255, 256, 257, 1023, 1024, M - 257, M - 256, M - 1,
+                           rng.choice(M, 22, replace=False)])
+    ors = (ora[0][rows], ora[1][rows], ora[2], ora[3])
+    plain = E.fp8_path_ref(*ors).astype(np.float64)
+    bias_bits = synthetic.to_bf16_bits(rng.standard_normal(N) * _rms(plain))
+    bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).to(dev[0].device)
+    y = w8.gemm(*dev)
+    torch.cuda.synchronize()
+    _check_values(bf16_to_f64(bf16_bits(y)[rows]), plain, f"{M}x{N}x{K} plain")
+    y = w8.gemm_ex(*dev, bias=bias, act="silu")
+    torch.cuda.synchronize()
+    _check_values(bf16_to_f64(bf16_bits(y)[rows]), E.fp8_path_ref(*ors, bias_bits=bias_bits, act="silu"),
+                  f"{M}x{N}x{K} bias silu")
+    s_out = float(np.float32(np.max(np.abs(plain)) / 300.0))
+    for act, b, bb in (("none", None, None), ("relu", bias, bias_bits)):
+        y = w8.gemm_ex(*dev, bias=b, act=act, out_scale=s_out)
+        torch.cuda.synchronize()
+        _check_fp8_codes(bits_u8(y)[rows], E.fp8_path_ref(*ors, bias_bits=bb, act=act, s_out=s_out),
+                         f"{M}x{N}x{K} fp8 out act={act}")
+
+
 def test_gemm_ex_options_off_equal_gemm():
     need_gpu()
     for fmt in ("e4m3fn", "int8"):

@@ -85,7 +85,8 @@ def test_fp8_few_tokens(M, N, K):
 # Regression: the two-waves-per-SIMD kernel refills an LDS stage while other waves of the
 # workgroup compute. A refill that starts before every wave has read the stage changes
 # results from run to run, so the same launch is repeated and must give identical bits.
-@pytest.mark.parametrize("M,N,K", [(256, 8193, 640), (2048, 4096, 1024), (512, 6144, 4096)])
+@pytest.mark.parametrize("M,N,K", [(256, 8193, 640), (2048, 4096, 1024), (512, 6144, 4096),
+                                   (2048, 28672, 512)])
 def test_fp8_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
