@@ -22,7 +22,7 @@
 // gives the same sum as long as W and X use the same one, so lane group g = l >> 4 takes
 // bytes [16g, 16g+16) and [64+16g, 64+16g+16): each 16-byte load instruction then reads
 // one contiguous 64-byte half-row per row. INT8 sums are exact in any order, so the INT8
-// result is bit-identical to the tiled kernel's.
+// result is bit-identical to the two-waves-per-SIMD kernel's.
 #include <type_traits>
 
 #include "common.h"

@@ -43,7 +43,7 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
 // Few-token form of launch_gemm: weights streamed by 16-, 32- or 64-row workgroups that
 // split K among their waves. It wins while the weights dominate the traffic: up to 64
 // tokens, and up to 128 on layers of at most 8192 outputs (measured crossover against the
-// tiled kernel at K = 4096).
+// 256-row tiled kernels at K = 4096).
 inline bool use_skinny(int64_t M, int64_t N) { return M <= 64 || (M <= 128 && N <= 8192); }
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
@@ -62,6 +62,10 @@ hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, ui
                                 hipStream_t st);
 hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
                              int64_t K, void* y, hipStream_t st);
+// INT8 form of the MXFP4 two-waves-per-SIMD kernel (256 x 128 tiles, 32x32x32 MFMAs).
+hipError_t launch_gemm_int8_pp(const void* xq, const float* sx, const void* wq, const float* sw,
+                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                               const Epilogue& ep);
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
                              const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t st);
