@@ -244,15 +244,21 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
     e = max(-127, min(127, e));
   }
   if ((threadIdx.x & 3) == 0) sc[c >> 2] = (uint8_t)(e + 127);
+  // gfx950's converter divides each bf16 of a pair by the scale's power of two (only the
+  // scale's exponent field is read: 2^e is passed as the fp32 pattern (e + 127) << 23),
+  // rounds half to even onto the E2M1 grid and saturates at 6, element 2i to the low
+  // nibble. The inputs' sign bits are ORed back in, so that values rounding to zero keep
+  // their sign (a no-op wherever the converter already keeps it).
+  const float scl = __uint_as_float((uint32_t)(e + 127) << 23);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t out = 0;
+  uint32_t out = 0, sgn = 0;
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2, w[0]), scl, 0);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2, w[1]), scl, 1);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2, w[2]), scl, 2);
+  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2, w[3]), scl, 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = e2m1_code(__builtin_ldexpf(bf16_lo(w[i]), -e));
-    const uint32_t hi = e2m1_code(__builtin_ldexpf(bf16_hi(w[i]), -e));
-    out |= (lo | (hi << 4)) << (8 * i);
-  }
-  reinterpret_cast<uint32_t*>(q)[c] = out;
+  for (int i = 0; i < 4; ++i) sgn |= (((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u)) << (8 * i);
+  reinterpret_cast<uint32_t*>(q)[c] = out | sgn;
 }
 
 hipError_t launch_quantize_mxfp4(const void* x, int64_t R, int64_t K, void* q, uint8_t* sc,
