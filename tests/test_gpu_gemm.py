@@ -181,12 +181,36 @@ def _int8_chain(xb, xcal, wb, alpha, what):
     assert np.array_equal(gy, oy), f"{what}: " + first_mismatch(gy, oy)
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 1024), (64, 256, 14336)])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 1024), (64, 256, 14336),
+                                   (513, 129, 1024), (260, 4100, 256), (2049, 1000, 512)])
 def test_int8_ragged(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
     xcal, _ = _xw(64, 1, K, K)
     _int8_chain(xb, xcal, wb, 0.5, f"{M}x{N}x{K}")
+
+
+# The INT8 GEMM shares the two-waves-per-SIMD schedule (and its stage refills) with the
+# MXFP4 one: repeated launches must give identical bits, equal to the oracle's.
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 1024), (512, 6144, 4096)])
+def test_int8_repeat_identical(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, 3 * M + N + K)
+    xq, sx = w8.quantize_per_token(to_dev_bf16(xb), "int8")
+    wq, sw = w8.quantize_weight_per_channel(to_dev_bf16(wb), "int8")
+    y0 = w8.gemm(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    ref = y0.clone()
+    for r in range(12):
+        w8.gemm(xq, sx, wq, sw, out=y0)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), ref.view(torch.int16)), f"{M}x{N}x{K}: run {r + 1} differs"
+    oxq, osx = Q.quantize_per_token_int8(xb)
+    owq, osw = Q.quantize_weight_per_channel_int8(wb)
+    rows = np.arange(0, M, max(1, M // 64))
+    oy = G.gemm_int8_ref(oxq[rows], osx[rows], owq, osw)
+    gy = bf16_bits(ref)[rows]
+    assert np.array_equal(gy, oy), f"{M}x{N}x{K}: " + first_mismatch(gy, oy)
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_CASES)
