@@ -60,7 +60,8 @@ def _parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16", "epilogue", "static", "all"])
+                   choices=["prefill", "msweep", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16", "epilogue",
+                            "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
@@ -385,6 +386,64 @@ def run_prefill(args, c: Ctx):
                       "gemm_source_sha256_16": gemm_source_hash()}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = prefill_cpu_baseline(layers, args.cpu_rows)
+    return rec
+
+
+# ----------------------------------------------------------------------------- token sweep
+MSWEEP_TOKENS = (2048, 4096, 8192)
+
+
+def run_msweep(args, c: Ctx):
+    """The four 8B linears at M = 2048, 4096 and 8192 tokens: the FP8 GEMM alone (weights
+    rotated over >600 MB, behind two untimed launches) and the whole quantize + GEMM pair,
+    to show how the fraction of the FP8 peak moves with the token count."""
+    import numpy as np
+    import synthetic
+    torch, w8, L, sh, stream = c.torch, c.w8, c.L, c.sh, c.stream
+    per_m, tot_flops, tot_gemm_s = [], 0.0, 0.0
+    for M in MSWEEP_TOKENS:
+        layers, flops, g_s, pair_s = [], 0.0, 0.0, 0.0
+        for i in range(len(synthetic.PREFILL_SHAPES)):
+            name, xb, wb = synthetic.prefill(i, M=M)
+            x = c.bf16(xb)
+            wq, sw = w8.quantize_weight_per_channel(c.bf16(wb))
+            del xb, wb
+            N, K = wq.shape
+            xq = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=c.dev)
+            sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
+            ws = [wq] + [wq.clone() for _ in range(max(4, math.ceil(600e6 / (N * K))) - 1)]
+
+            def quant():
+                c.check(L.w8a8_quantize_per_token(x.data_ptr(), M, K, 0, xq.data_ptr(), sx.data_ptr(), sh))
+
+            def gemm(w):
+                c.check(L.w8a8_gemm(xq.data_ptr(), sx.data_ptr(), w.data_ptr(), sw.data_ptr(), M, N, K, 0,
+                                    y.data_ptr(), sh))
+
+            quant()
+            for w in ws[:2]:
+                gemm(w)
+            g = _launch_mean_s(c, lambda i, ws=ws: gemm(ws[i]), len(ws))
+            pair = _launch_mean_s(c, lambda i, ws=ws: (quant(), gemm(ws[i])), len(ws))
+            f = 2.0 * M * N * K
+            layers.append({"layer": name, "N": N, "K": K, "gemm_us": round(g * 1e6, 1),
+                           "gemm_tflops": round(f / g / 1e12, 1), "quant_gemm_us": round(pair * 1e6, 1)})
+            flops, g_s, pair_s = flops + f, g_s + g, pair_s + pair
+            del ws, x, xq, y
+            torch.cuda.empty_cache()
+        per_m.append({"M": M, "gemm_tflops": round(flops / g_s / 1e12, 1),
+                      "gemm_frac": round(flops / g_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+                      "quant_gemm_tflops": round(flops / pair_s / 1e12, 1), "layers": layers})
+        tot_flops, tot_gemm_s = flops, g_s
+    value = per_m[-1]["gemm_tflops"]
+    rec = _base_record(args, "FP8 GEMM TFLOP/s at the 8B prefill linears vs tokens (largest M)", value,
+                       "TFLOP/s", tot_gemm_s * 1e3, "fp8_e4m3fn",
+                       {"workload": "8B-style FP8 W8A8 linears at M in {2048, 4096, 8192} tokens, "
+                                    "(K,N) in {(4096,6144),(4096,4096),(4096,28672),(14336,4096)}"})
+    rec["roofline"] = {"bound": "mfma", "achieved": round(value, 1), "peak": FP8_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(value / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    rec["sweep"] = per_m
     return rec
 
 
@@ -838,7 +897,7 @@ def main():
         print(json.dumps({"calibration_copy_bytes": n}), flush=True)
         return
     c = Ctx()
-    runs = {"prefill": run_prefill, "decode": run_decode, "blockscaled": run_blockscaled,
+    runs = {"prefill": run_prefill, "msweep": run_msweep, "decode": run_decode, "blockscaled": run_blockscaled,
             "epilogue": run_epilogue, "static": run_static,
             "mxfp4": run_mxfp4, "nvfp4": run_nvfp4, "w4a16": run_w4a16}
     names = list(runs) if args.workload == "all" else [args.workload]

@@ -75,10 +75,17 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int grp = wave >> 2, g4 = wave & 3;
   const int wm = g4, wn = grp;
+  // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that consecutive tiles
+  // run on one XCD and its L2, walking at most 8 row blocks of X before the next W panel.
   int b = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // tiles sharing W on one XCD
-  const int tm = b % tiles_m, tn = b / tiles_m;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  constexpr int GM = 8;
+  const int tiles_n = nb / tiles_m;
+  const int grp_m = b / (GM * tiles_n);
+  const int rows_g = min(tiles_m - grp_m * GM, GM);
+  const int rb = b - grp_m * GM * tiles_n;
+  const int tm = grp_m * GM + rb % rows_g, tn = rb / rows_g;
   const int m0 = tm * BM, n0 = tn * BN;
   const int S = ksteps * 8;                          // scale bytes per row
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
