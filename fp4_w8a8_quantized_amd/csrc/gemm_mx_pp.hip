@@ -76,11 +76,11 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   const int grp = wave >> 2, g4 = wave & 3;
   const int wm = g4, wn = grp;
   // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that consecutive tiles
-  // run on one XCD and its L2, walking at most 8 row blocks of X before the next W panel.
+  // run on one XCD and its L2, walking at most 4 row blocks of X before the next W panel.
   int b = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int tiles_n = nb / tiles_m;
   const int grp_m = b / (GM * tiles_n);
   const int rows_g = min(tiles_m - grp_m * GM, GM);

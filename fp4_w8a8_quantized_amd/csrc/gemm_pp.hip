@@ -105,14 +105,14 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   const int wm = WAVES_M == 4 ? g4 : (g4 & 1);
   const int wn = WAVES_M == 4 ? grp : grp * 2 + (g4 >> 1);
   // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that consecutive tiles
-  // run on one XCD and its L2. Consecutive tiles walk at most 8 row blocks of X, then the
-  // next W panel, so that the 32 tiles an XCD holds at once share 8 X blocks and 4 W
-  // panels (about 11 MB at K = 4096) rather than, at 8192 tokens, 32 X blocks and one
-  // panel (33 MB). Up to 2048 tokens this is the plain column-major order.
+  // run on one XCD and its L2. Consecutive tiles walk at most 4 row blocks of X, then the
+  // next W panel, so that the 32 tiles an XCD holds at once share 4 X blocks and 8 W
+  // panels (about 10 MB at K = 4096) rather than, in column-major order, all row blocks of
+  // X and a few panels (33 MB at 8192 tokens).
   int b = blockIdx.x;
   const int nb = gridDim.x;
   if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int tiles_n = nb / tiles_m;
   const int grp_m = b / (GM * tiles_n);
   const int rows_g = min(tiles_m - grp_m * GM, GM);
