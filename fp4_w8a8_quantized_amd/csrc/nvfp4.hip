@@ -130,10 +130,17 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave & 3, wn = wave >> 2;
+  // Workgroup ids are dealt round-robin over the 8 XCDs; remap so that consecutive tiles
+  // run on one XCD and its L2, walking at most 4 row blocks of X before the next W panel.
   int b = blockIdx.x;
   const int nb = gridDim.x;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);   // tiles sharing W on one XCD
-  const int tm = b % tiles_m, tn = b / tiles_m;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  constexpr int GM = 4;
+  const int tiles_n = nb / tiles_m;
+  const int grp_m = b / (GM * tiles_n);
+  const int rows_g = min(tiles_m - grp_m * GM, GM);
+  const int rb = b - grp_m * GM * tiles_n;
+  const int tm = grp_m * GM + rb % rows_g, tn = rb / rows_g;
   const int m0 = tm * kNvBM, n0 = tn * kNvBN;
   const int ksteps = K / kNvBK;
   const int64_t kb = K / 2, ks16 = K / 16;                 // bytes per row: codes, scales
