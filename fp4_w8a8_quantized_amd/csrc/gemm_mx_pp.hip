@@ -52,15 +52,15 @@ __device__ __forceinline__ void mx_barrier() { asm volatile("s_barrier" ::: "mem
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-template <bool I8, bool OF8>
+template <bool I8, bool OF8, int BN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
                   const uint8_t* __restrict__ wq, const void* __restrict__ swp, int M, int N,
                   int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store,
                   Epilogue ep) {
-  static_assert(I8 || !OF8, "the MXFP4 GEMM writes bf16");
-  constexpr int BM = kMxBM, BN = kMxBN;
-  constexpr int SM = 2, SN = 2;                     // 32 x 32 subtiles per wave (64 x 64)
+  static_assert(I8 || (!OF8 && BN == kMxBN), "the MXFP4 GEMM writes bf16 from 128-wide tiles");
+  constexpr int BM = kMxBM;
+  constexpr int SM = 2, SN = BN / 64;               // 32 x 32 subtiles per wave (64 x BN/2)
   constexpr int XT = BM * 128, WT = BN * 128;       // code bytes of a stage
   constexpr int SCX = I8 ? 0 : BM * 8, SCW = I8 ? 0 : BN * 8;   // MXFP4 scale bytes of a stage
   const uint8_t* __restrict__ sx = reinterpret_cast<const uint8_t*>(sxp);
@@ -119,7 +119,7 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   };
 
   const int fr = lane & 31, h = lane >> 5;
-  const int xrow0 = wm * 64, wrow0 = wn * 64;
+  const int xrow0 = wm * 64, wrow0 = wn * (BN / 2);
   int fo[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) fo[q] = mx_off(fr, 2 * q + h);
@@ -194,19 +194,25 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 
   // INT8: the epilogue's scales are loaded up front (before any direct-to-LDS load, so
   // group B's hand-counted waits see only its loads); their latency hides behind the loop.
-  // Lane l holds output row 32 i + (l & 31) and columns 32 j + 8 q + 4 (l >> 5) + r.
+  // The 192-wide tile cannot spare the column scales' registers during the loop and loads
+  // them after it. Lane l holds output row 32 i + (l & 31) and columns
+  // 32 j + 8 q + 4 (l >> 5) + r.
+  constexpr bool LATE_SN = (BN > 128);
   float esm[SM], esn[SN][4][4];
-  if constexpr (I8) {
-    const float* sxf = reinterpret_cast<const float*>(sxp);
+  auto load_esn = [&]() {
     const float* swf = reinterpret_cast<const float*>(swp);
-#pragma unroll
-    for (int i = 0; i < SM; ++i) esm[i] = sxf[min(m0 + xrow0 + 32 * i + fr, M - 1)];
 #pragma unroll
     for (int j = 0; j < SN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int r = 0; r < 4; ++r) esn[j][q][r] = swf[min(n0 + wrow0 + 32 * j + 8 * q + 4 * h + r, N - 1)];
+  };
+  if constexpr (I8) {
+    const float* sxf = reinterpret_cast<const float*>(sxp);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) esm[i] = sxf[min(m0 + xrow0 + 32 * i + fr, M - 1)];
+    if constexpr (!LATE_SN) load_esn();
   }
 
   // Prologue: B loads the codes of steps 0 and 1; A stores step 0's scales and holds step
@@ -269,6 +275,7 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   }
 
   // ---- epilogue
+  if constexpr (I8 && LATE_SN) load_esn();
   __builtin_amdgcn_s_waitcnt(mx_wait(0, 0));
   mx_barrier();
   if constexpr (I8) {
@@ -397,28 +404,40 @@ hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq, 
                              int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
   const int tiles_m = (int)((M + kMxBM - 1) / kMxBM);
   const int tiles_n = (int)((N + kMxBN - 1) / kMxBN);
-  hipLaunchKernelGGL((gemm_mx_pp_kernel<false, false>), dim3((unsigned)(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((gemm_mx_pp_kernel<false, false, kMxBN>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(kMxThreads), 0, st, (const uint8_t*)xq, (const void*)sx,
                      (const uint8_t*)wq, (const void*)sw, (int)M, (int)N, (int)(K / 2),
                      (int)(K / 256), y, tiles_m, (int)((N % 8) == 0), Epilogue{});
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_int8_pp(const void* xq, const float* sx, const void* wq, const float* sw,
-                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
-                               const Epilogue& ep) {
+template <int BN>
+hipError_t launch_i8(const void* xq, const float* sx, const void* wq, const float* sw, int64_t M,
+                     int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
   const int tiles_m = (int)((M + kMxBM - 1) / kMxBM);
-  const int tiles_n = (int)((N + kMxBN - 1) / kMxBN);
+  const int tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kMxThreads);
   if (ep.out_fp8)
-    hipLaunchKernelGGL((gemm_mx_pp_kernel<true, true>), grid, block, 0, st, (const uint8_t*)xq,
+    hipLaunchKernelGGL((gemm_mx_pp_kernel<true, true, BN>), grid, block, 0, st, (const uint8_t*)xq,
                        (const void*)sx, (const uint8_t*)wq, (const void*)sw, (int)M, (int)N,
                        (int)K, (int)(K / 128), y, tiles_m, (int)((N % 16) == 0), ep);
   else
-    hipLaunchKernelGGL((gemm_mx_pp_kernel<true, false>), grid, block, 0, st, (const uint8_t*)xq,
+    hipLaunchKernelGGL((gemm_mx_pp_kernel<true, false, BN>), grid, block, 0, st, (const uint8_t*)xq,
                        (const void*)sx, (const uint8_t*)wq, (const void*)sw, (int)M, (int)N,
                        (int)K, (int)(K / 128), y, tiles_m, (int)((N % 8) == 0), ep);
   return hipGetLastError();
+}
+
+// INT8 tile width: as for FP8, the width whose waves of workgroups over the 256 CUs cost
+// least, each weighted by its steady-state efficiency (192-wide tiles read fewer bytes per
+// MFMA: 64 x 96 wave tiles, 24 MFMAs on 20 fragment reads per step).
+hipError_t launch_gemm_int8_pp(const void* xq, const float* sx, const void* wq, const float* sw,
+                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                               const Epilogue& ep) {
+  const int64_t tm = (M + kMxBM - 1) / kMxBM;
+  auto cost = [&](int64_t bn, int64_t per_tile) { return ((tm * ((N + bn - 1) / bn) + 255) / 256) * per_tile; };
+  if (cost(192, 240) < cost(128, 194)) return launch_i8<192>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return launch_i8<128>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 }  // namespace w8a8

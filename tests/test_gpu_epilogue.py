@@ -155,6 +155,36 @@ def test_wide_tile_sampled(M, N, K):
                          f"{M}x{N}x{K} fp8 out act={act}")
 
 
+# INT8 layers of about 6000 outputs at 2048 tokens take 192-wide tiles (one wave of 256
+# workgroups instead of 1.5): bias and ReLU with bf16 and FP8 outputs bit for bit, SiLU
+# within the tolerance, on sampled rows including the first, last and tile-edge rows.
+@pytest.mark.parametrize("M,N,K", [(1999, 6001, 384), (2048, 6144, 256)])
+def test_int8_wide_tile_sampled(M, N, K):
+    need_gpu()
+    dev, ora = _setup("int8", M, N, K, 3 * M + N + K)
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.r_[0, 1, 255, 256, 257, 1023, 1024, M - 257, M - 256, M - 1,
+                           rng.choice(M, 22, replace=False)])
+    ors = (ora[0][rows], ora[1][rows], ora[2], ora[3])
+    plain = E.int8_path_values(*ors).astype(np.float64)
+    bias_bits = synthetic.to_bf16_bits(rng.standard_normal(N) * _rms(plain))
+    bias = torch.from_numpy(bias_bits.view(np.int16)).view(torch.bfloat16).to(dev[0].device)
+    y = w8.gemm_ex(*dev, bias=bias, act="relu")
+    torch.cuda.synchronize()
+    ref = E.int8_path_ref(*ors, bias_bits=bias_bits, act="relu")
+    assert np.array_equal(bf16_bits(y)[rows], ref), f"int8 {M}x{N}x{K} bias relu"
+    y = w8.gemm_ex(*dev, bias=bias, act="silu")
+    torch.cuda.synchronize()
+    _check_values(bf16_to_f64(bf16_bits(y)[rows]),
+                  E.int8_path_values(*ors, bias_bits=bias_bits, act="silu").astype(np.float64),
+                  f"int8 {M}x{N}x{K} bias silu")
+    s_out = np.float32(np.max(np.abs(plain)) / 300.0)
+    y = w8.gemm_ex(*dev, bias=bias, act="none", out_scale=float(s_out))
+    torch.cuda.synchronize()
+    ref = E.int8_path_ref(*ors, bias_bits=bias_bits, act="none", s_out=s_out)
+    assert np.array_equal(bits_u8(y)[rows], ref), f"int8 {M}x{N}x{K} fp8 out"
+
+
 def test_gemm_ex_options_off_equal_gemm():
     need_gpu()
     for fmt in ("e4m3fn", "int8"):

@@ -182,7 +182,8 @@ def _int8_chain(xb, xcal, wb, alpha, what):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 1024), (64, 256, 14336),
-                                   (513, 129, 1024), (260, 4100, 256), (2049, 1000, 512)])
+                                   (513, 129, 1024), (260, 4100, 256), (2049, 1000, 512),
+                                   (1999, 6001, 384), (2048, 6144, 256)])
 def test_int8_ragged(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
@@ -192,7 +193,7 @@ def test_int8_ragged(M, N, K):
 
 # The INT8 GEMM shares the two-waves-per-SIMD schedule (and its stage refills) with the
 # MXFP4 one: repeated launches must give identical bits, equal to the oracle's.
-@pytest.mark.parametrize("M,N,K", [(2048, 4096, 1024), (512, 6144, 4096)])
+@pytest.mark.parametrize("M,N,K", [(2048, 4096, 1024), (512, 6144, 4096), (2048, 6144, 1024)])
 def test_int8_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, 3 * M + N + K)
