@@ -6,9 +6,11 @@
 // activation quantization", Scale granularity; "FP8 and INT8 Inference" §6-9, the GEMM
 // epilogue; "Low-bit LLM Weights and Activations" §3.4).
 //
-// Few tokens (the weights dominate the traffic): the weight-streaming kernel of
-// gemm_skinny.hip. Otherwise the two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs
-// (gemm_pp.hip), INT8 on 32x32x32 MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
+// Up to 64 tokens (the weights dominate the traffic): the weight-streaming kernel of
+// gemm_skinny.hip. 65-128 tokens: gemm_mid.hip, whose workgroups hold every token row
+// against 16 or 64 weight rows (a 256-row tile would leave most CUs idle on 4096-wide
+// layers). Otherwise the two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip),
+// INT8 on 32x32x32 MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
 #include "common.h"
 #include "internal.h"
 
@@ -17,7 +19,8 @@ namespace w8a8 {
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                        const Epilogue& ep) {
-  if (use_skinny(M, N)) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  if (M <= 64) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  if (M <= 128) return launch_gemm_mid(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
   return launch_gemm_int8_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
 }

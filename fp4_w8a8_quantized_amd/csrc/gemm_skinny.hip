@@ -1,4 +1,4 @@
-// Few-token W8A8 GEMM (decode: M <= 64, or M <= 128 on layers of N <= 8192) on gfx950: the same result as the tiled GEMM,
+// Few-token W8A8 GEMM (decode: M <= 64) on gfx950: the same result as the tiled GEMM,
 // y = bf16( s_x[m] s_w[n] sum_k dec(xq) dec(wq) ) for FP8 and
 // y = bf16( fp32(fp32(acc_i32) s_x[m]) s_w[n] ) for INT8, but organised around streaming
 // the weights once at HBM rate.
@@ -210,11 +210,8 @@ static hipError_t launch_kind(const void* xq, const float* sx, const void* wq, c
     return wide ? launch_cfg<KIND, 2, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
                 : launch_cfg<KIND, 2, 8, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
   }
-  if (M <= 64) {
-    return wide ? launch_cfg<KIND, 4, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                : launch_cfg<KIND, 4, 4, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  }
-  return launch_cfg<KIND, 8, 4, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);   // M <= 128, N <= 8192
+  return wide ? launch_cfg<KIND, 4, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)     // M <= 64
+              : launch_cfg<KIND, 4, 4, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,

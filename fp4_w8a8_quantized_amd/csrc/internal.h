@@ -40,11 +40,13 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep);
 
-// Few-token form of launch_gemm: weights streamed by 16-, 32- or 64-row workgroups that
-// split K among their waves. It wins while the weights dominate the traffic: up to 64
-// tokens, and up to 128 on layers of at most 8192 outputs (measured crossover against the
-// 256-row tiled kernels at K = 4096).
-inline bool use_skinny(int64_t M, int64_t N) { return M <= 64 || (M <= 128 && N <= 8192); }
+// 65-128 tokens: every token row and 16 or 64 weight rows per workgroup; weights staged
+// in LDS a ring (16 or 8 K steps) ahead, X three steps ahead.
+hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
+                           int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                           const Epilogue& ep);
+// Up to 64 tokens: weights streamed by 16-, 32- or 64-row workgroups that split K among
+// their waves.
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                               const Epilogue& ep);

@@ -21,8 +21,10 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-2
 
-# tiled kernel (ragged and 16-aligned N) and the few-token kernel (narrow and wide)
-SHAPES = [(300, 549, 256), (256, 512, 384), (5, 130, 1152), (64, 10000, 256)]
+# tiled kernel (ragged and 16-aligned N), the few-token kernel (narrow and wide) and the
+# 65-128-token kernel (narrow and wide)
+SHAPES = [(300, 549, 256), (256, 512, 384), (5, 130, 1152), (64, 10000, 256), (100, 262, 512),
+          (128, 9001, 256)]
 
 
 def _inputs(M, N, K, seed):
