@@ -1,4 +1,4 @@
-// W8A8 GEMM for 65-128 tokens on gfx950, the same result as the other GEMMs:
+// W8A8 GEMM for 65-256 tokens on gfx950, the same result as the other GEMMs:
 //   FP8   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )
 //   INT8  y = epilogue( fp32(fp32(acc_i32) s_x[m]) s_w[n] )
 // ("FP8 and FP4 inference, SmoothQuant and activation quantization", Scale granularity;
@@ -6,8 +6,8 @@
 //
 // At these token counts a 256-row tile leaves most CUs idle on 4096-wide layers (32
 // tiles), and the few-token kernel, whose waves split K, re-reads X from L2 in 16-byte
-// loads one step ahead and waits on them. Here a workgroup of 4 waves owns all (up to 128)
-// token rows and 16 NW weight rows, so narrow layers still spread over every CU:
+// loads one step ahead and waits on them. Here a workgroup of 4 (8) waves owns all, up to
+// 128 (256), token rows and 16 NW weight rows, so narrow layers still spread over every CU:
 //  - each K step (128 bytes per row) of the 128 X rows and of the 16 NW W rows lands in
 //    LDS by direct-to-LDS loads (8 rows per 1 KB load, spread over the waves). The weights
 //    come from HBM and stream through a ring of 16 steps (8 for 64-row panels), issued one
@@ -26,8 +26,7 @@
 namespace w8a8 {
 namespace {
 
-constexpr int kMidStages = 4;                         // X ring (steps)
-constexpr int kMidRowsX = 128;
+constexpr int kMidStages = 4;                         // X ring (steps), 4 waves
 
 __device__ __forceinline__ int mid_off(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
@@ -47,23 +46,26 @@ constexpr int mid_wait(int vm, int lgkm) {
 
 __device__ __forceinline__ void mid_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int KIND, int NW, bool OF8>
-__global__ void __launch_bounds__(256)
+template <int KIND, int NW, bool OF8, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES)
 gemm_mid_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                 const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
                 int K, int ksteps, void* __restrict__ yp, Epilogue ep) {
-  constexpr int S = kMidStages, WS = NW >= 4 ? 8 : 16;   // X stages, W ring slots
+  constexpr int kMidRowsX = 32 * WAVES;              // token rows per workgroup
+  constexpr int S = WAVES == 4 ? kMidStages : 3;     // X stages
+  constexpr int WS = (NW >= 4 || WAVES > 4) ? 8 : 16;   // W ring slots (LDS <= 160 KB)
   constexpr int RW = 16 * NW;                        // weight rows per workgroup
   constexpr int XSTAGE = kMidRowsX * 128, WSLOT = RW * 128;
   constexpr int NDX = kMidRowsX / 8, NDW = RW / 8;   // 1 KB loads per step
-  constexpr int LMIN = NDX / 4 + NDW / 4;            // loads per wave per step, at least
+  constexpr int LMIN = NDX / WAVES + NDW / WAVES;    // loads per wave per step, at least
+  static_assert(S * XSTAGE + WS * WSLOT <= 160 * 1024, "LDS");
   static_assert(LMIN * (S - 2) < 64, "vmcnt holds at most 63");
   typedef typename std::conditional<KIND == 1, i32x4, f32x4>::type acc_t;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[S * XSTAGE + WS * WSLOT];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int n0 = blockIdx.x * RW;
+  const int n0 = blockIdx.x * RW, m0 = blockIdx.y * kMidRowsX;
   const int fr = lane & 15, g = lane >> 4;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
 
@@ -71,28 +73,28 @@ gemm_mid_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   // hand-counted waits below only see the latter.
   float esm[2], esn[NW][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) esm[i] = sx[min(32 * wave + 16 * i + fr, M - 1)];
+  for (int i = 0; i < 2; ++i) esm[i] = sx[min(m0 + 32 * wave + 16 * i + fr, M - 1)];
 #pragma unroll
   for (int j = 0; j < NW; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) esn[j][r] = sw[min(n0 + 16 * j + 4 * g + r, N - 1)];
 
-  // The loads of step ks: load d of its X rows (or W rows) is issued by wave d % 4; lane l
+  // The loads of step ks: load d of its X rows (or W rows) is issued by wave d % WAVES; lane l
   // fetches chunk (l & 7) ^ swizzle of row 8 d + (l >> 3) of the X stage (W slot). Steps
   // past the last re-fetch the last step into a stage or slot that is never read again.
   const uint32_t wlds0 = lds0 + S * XSTAGE;
   auto dma_x = [&](int ks) {
     const uint8_t* xb = xq + (size_t)min(ks, ksteps - 1) * 128;
 #pragma unroll
-    for (int d = wave; d < NDX; d += 4) {
+    for (int d = wave; d < NDX; d += WAVES) {
       const int r = 8 * d + (lane >> 3);
-      const uint32_t vo = (uint32_t)min(r, M - 1) * (uint32_t)K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+      const uint32_t vo = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
       mid_dma16(lds0 + (ks % S) * XSTAGE + d * 1024, vo, xb);
     }
   };
   auto dma_w = [&](int ks) {
     const uint8_t* wb = wq + (size_t)min(ks, ksteps - 1) * 128;
-    for (int d = wave; d < NDW; d += 4) {
+    for (int d = wave; d < NDW; d += WAVES) {
       const int r = 8 * d + (lane >> 3);
       const uint32_t vo = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
       mid_dma16(wlds0 + (ks % WS) * WSLOT + d * 1024, vo, wb);
@@ -158,7 +160,7 @@ gemm_mid_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     constexpr bool BIAS = decltype(bias_c)::value;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int m = 32 * wave + 16 * i + fr;
+      const int m = m0 + 32 * wave + 16 * i + fr;
       if (m >= M) continue;
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
@@ -200,34 +202,44 @@ gemm_mid_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   });
 }
 
-template <int KIND, int NW>
+template <int KIND, int NW, int WAVES>
 hipError_t launch_mid_cfg(const void* xq, const float* sx, const void* wq, const float* sw,
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep) {
-  const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW))), block(256);
+  const dim3 grid((unsigned)((N + 16 * NW - 1) / (16 * NW)), (unsigned)((M + 32 * WAVES - 1) / (32 * WAVES)));
+  const dim3 block(64 * WAVES);
   if (ep.out_fp8)
-    hipLaunchKernelGGL((gemm_mid_kernel<KIND, NW, true>), grid, block, 0, st, (const uint8_t*)xq,
+    hipLaunchKernelGGL((gemm_mid_kernel<KIND, NW, true, WAVES>), grid, block, 0, st, (const uint8_t*)xq,
                        sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, (int)(K / 128), y, ep);
   else
-    hipLaunchKernelGGL((gemm_mid_kernel<KIND, NW, false>), grid, block, 0, st, (const uint8_t*)xq,
+    hipLaunchKernelGGL((gemm_mid_kernel<KIND, NW, false, WAVES>), grid, block, 0, st, (const uint8_t*)xq,
                        sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, (int)(K / 128), y, ep);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// 16 weight rows per workgroup up to 8192 outputs (256 workgroups at 4096), 64 above
-// (224 workgroups at 14336, one round over the CUs).
+template <int KIND, int WAVES>
+hipError_t launch_mid_nw(const void* xq, const float* sx, const void* wq, const float* sw,
+                         int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                         const Epilogue& ep) {
+  if (N <= 4096) return launch_mid_cfg<KIND, 1, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  if (N <= 8192) return launch_mid_cfg<KIND, 2, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return launch_mid_cfg<KIND, 4, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+}
+
+// Weight rows per workgroup: 16, 32 or 64, the fewest that keep the workgroups to one
+// round over the 256 CUs (N <= 4096, 8192, 16384); every workgroup re-reads all of X, so
+// fewer, wider workgroups cost little. 4 waves up to 128 tokens, 8 up to 256 (a second row
+// of workgroups loses to the 256-row tiled kernels).
 hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                            const Epilogue& ep) {
-  if (M > kMidRowsX) return hipErrorInvalidValue;    // four waves of 32 token rows
-  const bool wide = N > 8192;
-  if (fmt == 1)
-    return wide ? launch_mid_cfg<1, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                : launch_mid_cfg<1, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  return wide ? launch_mid_cfg<0, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
-              : launch_mid_cfg<0, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  if (M <= 128)
+    return fmt == 1 ? launch_mid_nw<1, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                    : launch_mid_nw<0, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return fmt == 1 ? launch_mid_nw<1, 8>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                  : launch_mid_nw<0, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 }  // namespace w8a8

@@ -40,8 +40,8 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep);
 
-// 65-128 tokens: every token row and 16 or 64 weight rows per workgroup; weights staged
-// in LDS a ring (16 or 8 K steps) ahead, X three steps ahead.
+// 65-256 tokens: every token row and 16 or 64 weight rows per workgroup of 4 or 8 waves;
+// weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
 hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                            const Epilogue& ep);
