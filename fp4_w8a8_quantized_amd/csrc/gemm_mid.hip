@@ -8,17 +8,19 @@
 // tiles), and the few-token kernel, whose waves split K, re-reads X from L2 in 16-byte
 // loads one step ahead and waits on them. Here a workgroup of 4 (8) waves owns all, up to
 // 128 (256), token rows and 16 NW weight rows, so narrow layers still spread over every CU:
-//  - each K step (128 bytes per row) of the 128 X rows and of the 16 NW W rows lands in
-//    LDS by direct-to-LDS loads (8 rows per 1 KB load, spread over the waves). The weights
-//    come from HBM and stream through a ring of 16 steps (8 for 64-row panels), issued one
-//    ring ahead, so that each workgroup keeps 30-56 KB of them in flight; X, which the L2
-//    holds after its first
-//    reader, goes through a 4-stage ring three steps ahead. The weights of a step are
-//    always issued before its X, so one wait for the step's X covers both;
+//  - each K step (128 bytes per row) of the X rows and of the 16 NW W rows lands in LDS by
+//    direct-to-LDS loads (8 rows per 1 KB load, spread over the waves);
+//  - the weights come from HBM and stream through a ring of 16 steps (8 for 64-row panels
+//    or 8 waves), issued one ring ahead, so that each workgroup keeps 30-56 KB of them in
+//    flight; X, which the L2 holds after its first reader, goes through a ring of 4 (3)
+//    stages, issued three (two) steps ahead;
+//  - the weights of a step are always issued before its X, so one hand-counted wait for
+//    the step's X covers both;
 //  - wave w owns token rows 32 w .. 32 w + 31 (two 16-row subtiles) against every weight
-//    row, so no partial sums need to meet; its fragments come from the stage (lane l: row
-//    l & 15, 16-byte chunks g and g + 4, g = l >> 4, for both operands);
-//  - one barrier per step publishes the step's stage and retires the one read before.
+//    row, so no partial sums need to meet; its fragments come from LDS (lane l: row l & 15,
+//    16-byte chunks g and g + 4, g = l >> 4, for both operands);
+//  - one barrier per step publishes the step's stage and slot and retires the ones read
+//    before.
 // Rows past M or N re-read the last valid row; their results are never stored.
 #include "common.h"
 #include "internal.h"
@@ -26,7 +28,7 @@
 namespace w8a8 {
 namespace {
 
-constexpr int kMidStages = 4;                         // X ring (steps), 4 waves
+constexpr int kMidStages = 4;                         // X ring (steps) at 4 waves
 
 __device__ __forceinline__ int mid_off(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
