@@ -1,4 +1,4 @@
-// W8A8 GEMM for 65-256 tokens on gfx950, the same result as the other GEMMs:
+// W8A8 GEMM for 65-512 tokens on gfx950, the same result as the other GEMMs:
 //   FP8   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )
 //   INT8  y = epilogue( fp32(fp32(acc_i32) s_x[m]) s_w[n] )
 // ("FP8 and FP4 inference, SmoothQuant and activation quantization", Scale granularity;
@@ -6,8 +6,8 @@
 //
 // At these token counts a 256-row tile leaves most CUs idle on 4096-wide layers (32
 // tiles), and the few-token kernel, whose waves split K, re-reads X from L2 in 16-byte
-// loads one step ahead and waits on them. Here a workgroup of 4 (8) waves owns all, up to
-// 128 (256), token rows and 16 NW weight rows, so narrow layers still spread over every CU:
+// loads one step ahead and waits on them. Here a workgroup of 4 (8) waves owns up to 128
+// (256) token rows and 16 NW weight rows, so narrow layers still spread over every CU:
 //  - each K step (128 bytes per row) of the X rows and of the 16 NW W rows lands in LDS by
 //    direct-to-LDS loads (8 rows per 1 KB load, spread over the waves);
 //  - the weights come from HBM and stream through a ring of 16 steps (8 for 64-row panels
@@ -219,21 +219,30 @@ hipError_t launch_mid_cfg(const void* xq, const float* sx, const void* wq, const
   return hipGetLastError();
 }
 
-}  // namespace
-
 template <int KIND, int WAVES>
 hipError_t launch_mid_nw(const void* xq, const float* sx, const void* wq, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                          const Epilogue& ep) {
-  if (N <= 4096) return launch_mid_cfg<KIND, 1, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  if (N <= 8192) return launch_mid_cfg<KIND, 2, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  return launch_mid_cfg<KIND, 4, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  const int rw = mid_weight_rows(M, N);
+  if (rw == 16) return launch_mid_cfg<KIND, 1, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  if (rw == 32) return launch_mid_cfg<KIND, 2, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  if (rw == 64) return launch_mid_cfg<KIND, 4, WAVES>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return hipErrorInvalidValue;                      // the dispatcher sends no such shape
 }
 
-// Weight rows per workgroup: 16, 32 or 64, the fewest that keep the workgroups to one
-// round over the 256 CUs (N <= 4096, 8192, 16384); every workgroup re-reads all of X, so
-// fewer, wider workgroups cost little. 4 waves up to 128 tokens, 8 up to 256 (a second row
-// of workgroups loses to the 256-row tiled kernels).
+}  // namespace
+
+// Weight rows per workgroup: 16, 32 or 64, the fewest that keep the workgroups (one row of
+// them per 256 tokens) to one round over the 256 CUs; 0 if none does. Every workgroup
+// re-reads its tokens' X, so fewer, wider workgroups cost little.
+int mid_weight_rows(int64_t M, int64_t N) {
+  const int64_t rows = (M + 255) / 256;
+  for (int rw = 16; rw <= 64; rw *= 2)
+    if (rows * ((N + rw - 1) / rw) <= 256) return rw;
+  return 0;
+}
+
+// 4 waves up to 128 tokens, 8 waves (rows of workgroups 256 tokens tall) above.
 hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                            const Epilogue& ep) {

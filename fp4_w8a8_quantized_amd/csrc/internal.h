@@ -40,8 +40,11 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep);
 
-// 65-256 tokens: every token row and 16 or 64 weight rows per workgroup of 4 or 8 waves;
-// weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
+// 65-512 tokens: up to 256 token rows and 16, 32 or 64 weight rows per workgroup of 4 or 8
+// waves; weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
+// Weight rows per workgroup of launch_gemm_mid for an M x N output (16, 32 or 64), or 0
+// if even 64 would take more than one round of workgroups over the CUs.
+int mid_weight_rows(int64_t M, int64_t N);
 hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                            const Epilogue& ep);

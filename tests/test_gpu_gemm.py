@@ -66,17 +66,19 @@ def test_fp8_ragged(M, N, K):
     _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
 
 
-# Few-token paths (M <= 64: the weight-streaming kernel; 65 <= M <= 256: the kernel that
-# stages every token row and 16 or 64 weight rows per workgroup): every 16-row bucket
+# Few-token paths (M <= 64: the weight-streaming kernel; 65 <= M <= 512: the kernel that
+# stages up to 256 token rows and 16-64 weight rows per workgroup): every 16-row bucket
 # edge, N not a multiple of 4 or 16, one K step (most waves idle; the weight ring then
 # re-fetches the only step), K step counts below and above the ring depth, wide layers
 # with a ragged last workgroup (16, 32 and 64 weight rows per workgroup), the 8-wave form
-# (129-256 tokens), and the tiled kernel at M = 257 and above 16384 outputs.
+# (129-512 tokens, one or two rows of workgroups), and the tiled kernel where one round of
+# workgroups cannot cover the output (M = 513, or above 16384 outputs).
 SKINNY_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (65, 100, 2048),
                 (128, 130, 1152), (129, 257, 256), (2, 18, 14336), (16, 9000, 256),
                 (32, 8200, 384), (64, 10000, 1152), (128, 8193, 640), (97, 8209, 128),
                 (111, 4097, 2176), (128, 14336, 384), (200, 4100, 640), (256, 9000, 1152),
-                (160, 6144, 512), (257, 300, 256), (100, 20000, 256)]
+                (160, 6144, 512), (257, 300, 256), (100, 20000, 256), (400, 7000, 384),
+                (513, 1000, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_CASES)
@@ -91,7 +93,8 @@ def test_fp8_few_tokens(M, N, K):
 # results from run to run, so the same launch is repeated and must give identical bits.
 @pytest.mark.parametrize("M,N,K", [(256, 8193, 640), (2048, 4096, 1024), (512, 6144, 4096),
                                    (2048, 28672, 512), (128, 4096, 4096), (100, 14336, 1024),
-                                   (256, 4096, 2048), (200, 14336, 512)])
+                                   (256, 4096, 2048), (200, 14336, 512), (512, 4096, 1024),
+                                   (300, 4100, 512)])
 def test_fp8_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
@@ -199,7 +202,8 @@ def test_int8_ragged(M, N, K):
 # The INT8 GEMM shares the two-waves-per-SIMD schedule (and its stage refills) with the
 # MXFP4 one: repeated launches must give identical bits, equal to the oracle's.
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 1024), (512, 6144, 4096), (2048, 6144, 1024),
-                                   (128, 4096, 4096), (100, 14336, 1024), (256, 4096, 2048)])
+                                   (128, 4096, 4096), (100, 14336, 1024), (256, 4096, 2048),
+                                   (512, 4096, 1024)])
 def test_int8_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, 3 * M + N + K)
