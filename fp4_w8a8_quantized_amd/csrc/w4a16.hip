@@ -215,6 +215,7 @@ hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, ui
 
 hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
                              int64_t K, void* y, hipStream_t st) {
+  if (use_w4a16_mid(M, N, K)) return launch_gemm_w4a16_mid(x, wq, sc, M, N, K, y, st);
   for (int64_t m0 = 0; m0 < M; m0 += 128) {
     const int64_t mr = M - m0 < 128 ? M - m0 : 128;
     const hipError_t e = launch_w4a16_slice(reinterpret_cast<const uint16_t*>(x) + m0 * K, wq, sc, mr,

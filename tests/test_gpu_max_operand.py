@@ -169,7 +169,7 @@ def test_nvfp4_weight_at_limit(raw):
                NV.gemm_nvfp4_ref(xq, sx, gx, wq[cols], sw[cols], gw), f"nvfp4 {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M", [1, 16])
+@pytest.mark.parametrize("M", [1, 16, 100])
 def test_w4a16_weight_at_limit(raw, M):
     """W 131072 x 32768 INT4 (2^31 packed bytes, every nibble incl. -8) with fp16 scales."""
     need_gpu()

@@ -65,10 +65,18 @@ def _gemm_compare(xb, wb, what):
     assert ok, f"{what}: worst error / bound = {worst:.3f}"
 
 
-# every 16-row subtile edge, M above 128 (slices), N not a multiple of 4 or 16, one group
+# every 16-row subtile edge, M above 128 (slices), N not a multiple of 4 or 16, one group;
+# K a multiple of 1024 above 32 tokens (16 above 8192 outputs) takes the LDS-staged kernel:
+# each of its launch shapes (32, 64 or 128 token rows x 16, 32 or 64 weight rows), one to
+# three rows of workgroups, ragged M and N
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (5, 7, 256), (16, 130, 384), (17, 64, 1024),
                                    (33, 300, 512), (64, 4099, 256), (100, 96, 2048), (128, 257, 640),
-                                   (129, 33, 256), (300, 200, 384), (2, 9000, 1152)])
+                                   (129, 33, 256), (300, 200, 384), (2, 9000, 1152),
+                                   (100, 1001, 2048), (129, 77, 1024), (300, 4100, 1024),
+                                   (48, 20000, 1024), (200, 3001, 1024), (1, 4096, 1024),
+                                   (16, 4096, 2048), (257, 9000, 3072), (17, 20000, 1024),
+                                   (17, 9000, 1024), (33, 4100, 1024), (33, 9000, 1024),
+                                   (65, 7000, 1024), (32, 4096, 1024)])
 def test_gemm_w4a16_ragged(M, N, K):
     need_gpu()
     rng = np.random.default_rng(M * 13 + N * 3 + K)
