@@ -187,6 +187,24 @@ def test_w4a16_weight_at_limit(raw, M):
                W.gemm_w4a16_ref(xb, wq[cols], s[cols]), f"w4a16 {M}x{N}x{K}")
 
 
+def test_w4a16_activation_at_limit(raw):
+    """X bf16 131072 x 8192 (2^31 bytes, |x| in [2^-7, 2)) against a 16-row INT4 weight: the
+    LDS-staged kernel at its largest activation offsets."""
+    need_gpu()
+    M, N, K = 131072, 16, 8192
+    rng = _rng(8)
+    xb = ((raw.view(np.uint16) & np.uint16(0x83FF)) | np.uint16(0x3C00)).reshape(M, K)
+    wq = synthetic.random_bytes(N * K // 2, synthetic.seed(9, 8, 2)).reshape(N, K // 2)
+    s = np.exp2(rng.uniform(-10, -4, (N, K // 128))).astype(np.float16)
+    dx = to_dev_bf16(xb)
+    y = w8.gemm_w4a16(dx, to_dev(wq), to_dev(s))
+    torch.cuda.synchronize()
+    del dx
+    rows = _sample(M, rng)
+    _check_tol(bf16_to_f64(y[torch.from_numpy(rows).to(y.device)]),
+               W.gemm_w4a16_ref(xb[rows], wq, s), f"w4a16 {M}x{N}x{K}")
+
+
 def test_quantize_per_token_at_limit(raw):
     """X bf16 65536 x 16384 (2^31 bytes): codes and scales of sampled rows bit for bit."""
     need_gpu()
