@@ -119,8 +119,8 @@ __device__ __forceinline__ u32x4 nv_dequant8(uint32_t w, _Float16 mul) {
 // subtiles of 16x16), K step 64. Every thread owns a share of each step's codes and scales
 // (X row t/2, half t%2: 32 elements, two blocks; W row t/4, quarter t%4: 16 elements, one
 // block). Step k: fragments and MFMAs for the first K32 half of stage k%2; dequantization
-// of step k+1's share into the other stage, then the fetch of step k+2's share into the
-// freed registers; the second K32 half; one barrier.
+// of step k+1's share into the other stage, then the fetch of step k+3's share into the
+// freed registers (two sets in flight); the second K32 half; one barrier.
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                   const float* __restrict__ gx, const uint8_t* __restrict__ wq,
@@ -156,26 +156,30 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   const uint8_t* wrow = wq + (int64_t)wr * kb + 8 * wq4;
   const uint8_t* wsrow = ws + (int64_t)wr * ks16 + wq4;
 
-  u32x4 xa;
-  u32x2 wa;
-  uint32_t xsc, wsc;
-  auto fetch = [&](int k) {
-    xa = *reinterpret_cast<const u32x4*>(xrow + 32 * k);
-    xsc = *reinterpret_cast<const uint16_t*>(xsrow + 4 * k);
-    wa = *reinterpret_cast<const u32x2*>(wrow + 32 * k);
-    wsc = wsrow[4 * k];
+  // One step's share of codes and scales, held in registers between its fetch and its
+  // dequantization into a stage.
+  struct Raw {
+    u32x4 xa;
+    u32x2 wa;
+    uint32_t xsc, wsc;
   };
-  auto store = [&](int stage) {
+  auto fetch = [&](Raw& r, int k) {
+    r.xa = *reinterpret_cast<const u32x4*>(xrow + 32 * k);
+    r.xsc = *reinterpret_cast<const uint16_t*>(xsrow + 4 * k);
+    r.wa = *reinterpret_cast<const u32x2*>(wrow + 32 * k);
+    r.wsc = wsrow[4 * k];
+  };
+  auto store = [&](const Raw& r, int stage) {
     uint8_t* X = lds + stage * kNvStage;
     uint8_t* W = X + kNvXT;
-    const _Float16 x0 = nv_block_mul(xsc & 0xFFu, zx), x1 = nv_block_mul((xsc >> 8) & 0xFFu, zx);
-    const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w};
+    const _Float16 x0 = nv_block_mul(r.xsc & 0xFFu, zx), x1 = nv_block_mul((r.xsc >> 8) & 0xFFu, zx);
+    const uint32_t xw[4] = {r.xa.x, r.xa.y, r.xa.z, r.xa.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c)                            // chunk 4 xh + c: 8 elements
       *reinterpret_cast<u32x4*>(X + nv_off(xr_l, 4 * xh + c)) = nv_dequant8(xw[c], c < 2 ? x0 : x1);
-    const _Float16 w0 = nv_block_mul(wsc & 0xFFu, zw);
-    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4)) = nv_dequant8(wa.x, w0);
-    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4 + 1)) = nv_dequant8(wa.y, w0);
+    const _Float16 w0 = nv_block_mul(r.wsc & 0xFFu, zw);
+    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4)) = nv_dequant8(r.wa.x, w0);
+    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4 + 1)) = nv_dequant8(r.wa.y, w0);
   };
 
   f32x4 acc[4][4];
@@ -203,19 +207,28 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
         acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xf[i], acc[j][i], 0, 0, 0);
   };
 
-  fetch(0);
-  store(0);
-  if (ksteps > 1) fetch(1);
+  // Step k reads stage k % 2 and dequantizes step k + 1 (fetched two steps earlier, in
+  // register set (k + 1) % 2) into the other stage, then fetches step k + 3 into the set it
+  // freed. The loop is unrolled by two so that each set is a fixed set of registers.
+  Raw r0, r1;
+  fetch(r0, 0);
+  store(r0, 0);
+  if (ksteps > 1) fetch(r1, 1);
+  if (ksteps > 2) fetch(r0, 2);
   __syncthreads();
-  for (int k = 0; k < ksteps; ++k) {
+  auto step = [&](int k, Raw& next) {
     const uint8_t* X = lds + (k & 1) * kNvStage;
     half(X, 0);
     if (k + 1 < ksteps) {
-      store((k + 1) & 1);
-      if (k + 2 < ksteps) fetch(k + 2);
+      store(next, (k + 1) & 1);
+      if (k + 3 < ksteps) fetch(next, k + 3);
     }
     half(X, 1);
     __syncthreads();
+  };
+  for (int k = 0; k < ksteps; k += 2) {
+    step(k, r1);
+    if (k + 1 < ksteps) step(k + 1, r0);
   }
 
   // Epilogue: y = bf16(acc * g_x g_w), staged through LDS as whole rows.
