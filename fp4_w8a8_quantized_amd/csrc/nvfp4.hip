@@ -83,10 +83,10 @@ __global__ __launch_bounds__(256) void nv_quant_kernel(const u32x4* __restrict__
 }
 
 // --------------------------------------------------------------------------------- GEMM
-constexpr int kNvBM = 256, kNvBN = 128, kNvBK = 64;      // K step: 64 elements
+constexpr int kNvBM = 256, kNvBK = 64;                   // K step: 64 elements
 constexpr int kNvThreads = 512;
 constexpr int kNvRow = kNvBK * 2;                         // fp16 row of a stage: 128 bytes
-constexpr int kNvXT = kNvBM * kNvRow, kNvWT = kNvBN * kNvRow, kNvStage = kNvXT + kNvWT;
+constexpr int kNvXT = kNvBM * kNvRow;
 
 // 16-byte chunk c of fp16 row r sits at slot c ^ ((r >> 1) & 7): the MFMA fragment reads
 // (16 rows x chunks g or g + 4) and the dequantizer's row writes are free of bank conflicts.
@@ -115,18 +115,22 @@ __device__ __forceinline__ u32x4 nv_dequant8(uint32_t w, _Float16 mul) {
                __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
 }
 
-// A 256 x 128 tile per workgroup of 8 waves (two per SIMD), wave tile 64 x 64 (4 x 4
-// subtiles of 16x16), K step 64. Every thread owns a share of each step's codes and scales
-// (X row t/2, half t%2: 32 elements, two blocks; W row t/4, quarter t%4: 16 elements, one
-// block). Step k: fragments and MFMAs for the first K32 half of stage k%2; dequantization
+// A 256 x BN tile per workgroup of 8 waves (two per SIMD), wave tile 64 x BN/2 (4 x BN/32
+// subtiles of 16x16), K step 64; BN = 256 halves the LDS bytes read per MFMA for the
+// weights. Every thread owns a share of each step's codes and scales (X row t/2, half t%2:
+// 32 elements, two blocks; W at BN = 128 row t/4, quarter t%4: 16 elements, one block; at
+// BN = 256 like X). Step k: fragments and MFMAs for the first K32 half of stage k%2; dequantization
 // of step k+1's share into the other stage, then the fetch of step k+3's share into the
 // freed registers (two sets in flight); the second K32 half; one barrier.
+template <int BN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
                   const float* __restrict__ gx, const uint8_t* __restrict__ wq,
                   const uint8_t* __restrict__ ws, const float* __restrict__ gw, int M, int N, int K,
                   uint16_t* __restrict__ y, int tiles_m, int vec_store) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kNvStage];
+  constexpr bool WIDE = BN == 256;                         // 64 x 128 wave tiles
+  constexpr int STAGE = kNvXT + BN * kNvRow, NJ = BN / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave & 3, wn = wave >> 2;
@@ -141,7 +145,7 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   const int rows_g = min(tiles_m - grp_m * GM, GM);
   const int rb = b - grp_m * GM * tiles_n;
   const int tm = grp_m * GM + rb % rows_g, tn = rb / rows_g;
-  const int m0 = tm * kNvBM, n0 = tn * kNvBN;
+  const int m0 = tm * kNvBM, n0 = tn * BN;
   const int ksteps = K / kNvBK;
   const int64_t kb = K / 2, ks16 = K / 16;                 // bytes per row: codes, scales
 
@@ -149,61 +153,71 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   const float zx = g_x > 42.f ? 1.f / g_x : 0.f, zw = g_w > 42.f ? 1.f / g_w : 0.f;
 
   // this thread's rows (past M or N: the last row again; never stored)
-  const int xr_l = t >> 1, xh = t & 1, wr_l = t >> 2, wq4 = t & 3;
+  const int xr_l = t >> 1, xh = t & 1, wr_l = WIDE ? t >> 1 : t >> 2, wq4 = WIDE ? t & 1 : t & 3;
   const int xr = min(m0 + xr_l, M - 1), wr = min(n0 + wr_l, N - 1);
   const uint8_t* xrow = xq + (int64_t)xr * kb + 16 * xh;
   const uint8_t* xsrow = xs + (int64_t)xr * ks16 + 2 * xh;
-  const uint8_t* wrow = wq + (int64_t)wr * kb + 8 * wq4;
-  const uint8_t* wsrow = ws + (int64_t)wr * ks16 + wq4;
+  const uint8_t* wrow = wq + (int64_t)wr * kb + (WIDE ? 16 : 8) * wq4;
+  const uint8_t* wsrow = ws + (int64_t)wr * ks16 + (WIDE ? 2 : 1) * wq4;
+  typedef typename std::conditional<WIDE, u32x4, u32x2>::type wv_t;
 
   // One step's share of codes and scales, held in registers between its fetch and its
   // dequantization into a stage.
   struct Raw {
     u32x4 xa;
-    u32x2 wa;
+    wv_t wa;
     uint32_t xsc, wsc;
   };
   auto fetch = [&](Raw& r, int k) {
     r.xa = *reinterpret_cast<const u32x4*>(xrow + 32 * k);
     r.xsc = *reinterpret_cast<const uint16_t*>(xsrow + 4 * k);
-    r.wa = *reinterpret_cast<const u32x2*>(wrow + 32 * k);
-    r.wsc = wsrow[4 * k];
+    r.wa = *reinterpret_cast<const wv_t*>(wrow + 32 * k);
+    if constexpr (WIDE) r.wsc = *reinterpret_cast<const uint16_t*>(wsrow + 4 * k);
+    else r.wsc = wsrow[4 * k];
   };
   auto store = [&](const Raw& r, int stage) {
-    uint8_t* X = lds + stage * kNvStage;
+    uint8_t* X = lds + stage * STAGE;
     uint8_t* W = X + kNvXT;
     const _Float16 x0 = nv_block_mul(r.xsc & 0xFFu, zx), x1 = nv_block_mul((r.xsc >> 8) & 0xFFu, zx);
     const uint32_t xw[4] = {r.xa.x, r.xa.y, r.xa.z, r.xa.w};
 #pragma unroll
     for (int c = 0; c < 4; ++c)                            // chunk 4 xh + c: 8 elements
       *reinterpret_cast<u32x4*>(X + nv_off(xr_l, 4 * xh + c)) = nv_dequant8(xw[c], c < 2 ? x0 : x1);
-    const _Float16 w0 = nv_block_mul(r.wsc & 0xFFu, zw);
-    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4)) = nv_dequant8(r.wa.x, w0);
-    *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4 + 1)) = nv_dequant8(r.wa.y, w0);
+    if constexpr (WIDE) {
+      const _Float16 w0 = nv_block_mul(r.wsc & 0xFFu, zw), w1 = nv_block_mul((r.wsc >> 8) & 0xFFu, zw);
+      const uint32_t ww[4] = {r.wa.x, r.wa.y, r.wa.z, r.wa.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 4 * wq4 + c)) = nv_dequant8(ww[c], c < 2 ? w0 : w1);
+    } else {
+      const _Float16 w0 = nv_block_mul(r.wsc & 0xFFu, zw);
+      *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4)) = nv_dequant8(r.wa.x, w0);
+      *reinterpret_cast<u32x4*>(W + nv_off(wr_l, 2 * wq4 + 1)) = nv_dequant8(r.wa.y, w0);
+    }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[NJ][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, g = lane >> 4;
-  const int xrow0 = wm * 64, wrow0 = wn * 64;
+  const int xrow0 = wm * 64, wrow0 = wn * (BN / 2);
   // One K32 half of a step: fragments from the stage, then 16 MFMAs.
   auto half = [&](const uint8_t* X, int s) {
     const uint8_t* W = X + kNvXT;
-    f16x8 xf[4], wf[4];
+    f16x8 xf[4], wf[NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       xf[i] = *reinterpret_cast<const f16x8*>(X + nv_off(xrow0 + 16 * i + fr, 4 * s + g));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
       wf[j] = *reinterpret_cast<const f16x8*>(W + nv_off(wrow0 + 16 * j + fr, 4 * s + g));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xf[i], acc[j][i], 0, 0, 0);
   };
 
@@ -217,7 +231,7 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
   if (ksteps > 2) fetch(r0, 2);
   __syncthreads();
   auto step = [&](int k, Raw& next) {
-    const uint8_t* X = lds + (k & 1) * kNvStage;
+    const uint8_t* X = lds + (k & 1) * STAGE;
     half(X, 0);
     if (k + 1 < ksteps) {
       store(next, (k + 1) & 1);
@@ -231,10 +245,35 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
     if (k + 1 < ksteps) step(k + 1, r0);
   }
 
-  // Epilogue: y = bf16(acc * g_x g_w), staged through LDS as whole rows.
-  constexpr int RS = kNvBN * 2 + 16;
-  static_assert(kNvBM * RS <= 2 * kNvStage, "output tile must fit in the stage LDS");
   const float gxw = g_x * g_w;
+  if constexpr (WIDE) {
+    // Epilogue straight from registers (the 256 x 256 output tile does not fit the stage
+    // LDS): lane l holds output row 16 i + (l & 15) and columns 16 j + 4 (l >> 4) + r.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + xrow0 + 16 * i + fr;
+      if (m >= M) continue;
+      uint16_t* yr = y + (size_t)m * N;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wrow0 + 16 * j + 4 * g;
+        if (n >= N) continue;
+        const uint32_t o[2] = {pack_bf16x2(acc[j][i][0] * gxw, acc[j][i][1] * gxw),
+                               pack_bf16x2(acc[j][i][2] * gxw, acc[j][i][3] * gxw)};
+        if ((N & 3) == 0) {
+          *reinterpret_cast<u32x2*>(yr + n) = u32x2{o[0], o[1]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) yr[n + r] = (uint16_t)((o[r >> 1] >> (16 * (r & 1))) & 0xFFFFu);
+        }
+      }
+    }
+    return;
+  }
+  // Epilogue: y = bf16(acc * g_x g_w), staged through LDS as whole rows.
+  constexpr int RS = BN * 2 + 16;
+  static_assert(WIDE || kNvBM * RS <= 2 * STAGE, "output tile must fit in the stage LDS");
   // lane l holds output row 16 i + (l & 15) and columns 16 j + 4 (l >> 4) + r
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -248,7 +287,7 @@ gemm_nvfp4_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs
     }
   }
   __syncthreads();
-  constexpr int CPR = kNvBN / 8;                           // 16-byte chunks per output row
+  constexpr int CPR = BN / 8;                           // 16-byte chunks per output row
   for (int c = t; c < kNvBM * CPR; c += kNvThreads) {
     const int rl = c / CPR, ch = c - rl * CPR;
     const int m = m0 + rl, n = n0 + ch * 8;
@@ -298,11 +337,19 @@ hipError_t launch_quantize_nvfp4(const void* x, int64_t R, int64_t K, bool given
 hipError_t launch_gemm_nvfp4(const void* xq, const uint8_t* xs, const float* gx, const void* wq,
                              const uint8_t* ws, const float* gw, int64_t M, int64_t N, int64_t K,
                              void* y, hipStream_t st) {
-  const int tiles_m = (int)((M + kNvBM - 1) / kNvBM);
-  const int tiles_n = (int)((N + kNvBN - 1) / kNvBN);
-  hipLaunchKernelGGL(gemm_nvfp4_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kNvThreads), 0, st,
-                     (const uint8_t*)xq, xs, gx, (const uint8_t*)wq, ws, gw, (int)M, (int)N, (int)K,
-                     (uint16_t*)y, tiles_m, (int)((N % 8) == 0));
+  // 256 x 256 tiles where they cost less: a round of them over the 256 CUs measured 1.63
+  // times a round of 256 x 128 tiles (8192^3: 882 against 1077 us in all).
+  const int64_t tiles_m = (M + kNvBM - 1) / kNvBM;
+  const int64_t wide = tiles_m * ((N + 255) / 256), narrow = tiles_m * ((N + 127) / 128);
+  const bool use_wide = ((wide + 255) / 256) * 163 < ((narrow + 255) / 256) * 100;
+  if (use_wide)
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<256>, dim3((unsigned)wide), dim3(kNvThreads), 0, st,
+                       (const uint8_t*)xq, xs, gx, (const uint8_t*)wq, ws, gw, (int)M, (int)N, (int)K,
+                       (uint16_t*)y, (int)tiles_m, (int)((N % 8) == 0));
+  else
+    hipLaunchKernelGGL(gemm_nvfp4_kernel<128>, dim3((unsigned)narrow), dim3(kNvThreads), 0, st,
+                       (const uint8_t*)xq, xs, gx, (const uint8_t*)wq, ws, gw, (int)M, (int)N, (int)K,
+                       (uint16_t*)y, (int)tiles_m, (int)((N % 8) == 0));
   return hipGetLastError();
 }
 

@@ -94,8 +94,10 @@ def _gemm_compare(xb, wb, what, rows=None):
     assert ok, f"{what}: worst error / bound = {worst:.3f}"
 
 
+# the 256 x 128 tile throughout, and the 256 x 256 tile (ragged M and N) at 2000 x 8000
 @pytest.mark.parametrize("M,N_,K", [(1, 1, 64), (17, 130, 128), (300, 549, 256), (257, 129, 640),
-                                    (64, 256, 4096), (513, 1000, 1024)])
+                                    (64, 256, 4096), (513, 1000, 1024), (2000, 8000, 128),
+                                    (2048, 8190, 192)])
 def test_gemm_nvfp4_ragged(M, N_, K):
     need_gpu()
     xb = _x(M, K, M * 31 + N_ * 7 + K)
