@@ -10,10 +10,11 @@
 // (256) token rows and 16 NW weight rows, so narrow layers still spread over every CU:
 //  - each K step (128 bytes per row) of the X rows and of the 16 NW W rows lands in LDS by
 //    direct-to-LDS loads (8 rows per 1 KB load, spread over the waves);
-//  - the weights come from HBM and stream through a ring of 16 steps (8 for 64-row panels
-//    or 8 waves), issued one ring ahead, so that each workgroup keeps 30-56 KB of them in
-//    flight; X, which the L2 holds after its first reader, goes through a ring of 4 (3)
-//    stages, issued three (two) steps ahead;
+//  - the weights come from HBM and stream through a ring of up to 16 steps (8 for 64-row
+//    panels or 8 waves, 4 for 64-row panels at 8 waves), issued one ring ahead, so that
+//    each workgroup keeps 30-56 KB of them in flight; X, which the L2 holds after its
+//    first reader, goes through a ring of 4 stages (6 at 4 waves on 16 weight rows),
+//    issued three (five) steps ahead;
 //  - the weights of a step are always issued before its X, so one hand-counted wait for
 //    the step's X covers both;
 //  - wave w owns token rows 32 w .. 32 w + 31 (two 16-row subtiles) against every weight
@@ -27,8 +28,6 @@
 
 namespace w8a8 {
 namespace {
-
-constexpr int kMidStages = 4;                         // X ring (steps) at 4 waves
 
 __device__ __forceinline__ int mid_off(int row, int chunk) {
   return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
@@ -54,10 +53,15 @@ gemm_mid_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                 const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
                 int K, int ksteps, void* __restrict__ yp, Epilogue ep) {
   constexpr int kMidRowsX = 32 * WAVES;              // token rows per workgroup
-  constexpr int S = WAVES == 4 ? kMidStages : 3;     // X stages
-  constexpr int WS = (NW >= 4 || WAVES > 4) ? 8 : 16;   // W ring slots (LDS <= 160 KB)
+  // X stages: 6 for 4 waves on 16 weight rows, else 4 (measured against 3 at 8 waves:
+  // 400 x 4096 x 14336 68.6 -> 54.3 us; 6 at 4 waves on 64 weight rows was slower).
+  constexpr int S = (WAVES == 4 && NW == 1) ? 6 : 4;
   constexpr int RW = 16 * NW;                        // weight rows per workgroup
   constexpr int XSTAGE = kMidRowsX * 128, WSLOT = RW * 128;
+  constexpr int WS0 = (NW >= 4 || WAVES > 4) ? 8 : 16;
+  constexpr int WSFIT = (160 * 1024 - S * XSTAGE) / WSLOT;
+  constexpr int WS = WSFIT < WS0 ? WSFIT : WS0;      // W ring slots (LDS <= 160 KB)
+  static_assert(WS >= S, "weights issued no later than the X of their step");
   constexpr int NDX = kMidRowsX / 8, NDW = RW / 8;   // 1 KB loads per step
   constexpr int LMIN = NDX / WAVES + NDW / WAVES;    // loads per wave per step, at least
   static_assert(S * XSTAGE + WS * WSLOT <= 160 * 1024, "LDS");
