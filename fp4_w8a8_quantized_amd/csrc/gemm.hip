@@ -8,7 +8,7 @@
 //
 // Up to 64 tokens (the weights dominate the traffic): the weight-streaming kernel of
 // gemm_skinny.hip. 65-512 tokens, where one round of workgroups covers the output:
-// gemm_mid.hip, whose workgroups hold up to 256 token rows against 16-64 weight rows (a
+// gemm_mid.hip, whose workgroups hold up to 256 token rows against 16-128 weight rows (a
 // 256-row tile would leave most CUs idle on 4096-wide layers). Otherwise the
 // two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8 on 32x32x32
 // MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).

@@ -40,10 +40,10 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep);
 
-// 65-512 tokens: up to 256 token rows and 16, 32 or 64 weight rows per workgroup of 4 or 8
+// 65-512 tokens: up to 256 token rows and 16-128 weight rows per workgroup of 4 or 8
 // waves; weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
-// Weight rows per workgroup of launch_gemm_mid for an M x N output (16, 32 or 64), or 0
-// if even 64 would take more than one round of workgroups over the CUs.
+// Weight rows per workgroup of launch_gemm_mid for an M x N output (16, 32, 64, or 128 up
+// to 128 tokens), or 0 if even the widest would take more than one round of workgroups.
 int mid_weight_rows(int64_t M, int64_t N);
 hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
@@ -67,8 +67,8 @@ hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, ui
                                 hipStream_t st);
 hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
                              int64_t K, void* y, hipStream_t st);
-// W4A16 above 16 tokens with K a multiple of 1024: 128 token rows and 16-64 weight rows per
-// workgroup, both staged in LDS one group per K step.
+// W4A16 above 32 tokens (16 above 8192 outputs) with K a multiple of 1024: 32-128 token rows
+// and 16-64 weight rows per workgroup, both staged in LDS one group per K step.
 bool use_w4a16_mid(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w4a16_mid(const void* x, const void* wq, const uint16_t* sc, int64_t M,
                                  int64_t N, int64_t K, void* y, hipStream_t st);

@@ -67,17 +67,19 @@ def test_fp8_ragged(M, N, K):
 
 
 # Few-token paths (M <= 64: the weight-streaming kernel; 65 <= M <= 512: the kernel that
-# stages up to 256 token rows and 16-64 weight rows per workgroup): every 16-row bucket
+# stages up to 256 token rows and 16-128 weight rows per workgroup): every 16-row bucket
 # edge, N not a multiple of 4 or 16, one K step (most waves idle; the weight ring then
 # re-fetches the only step), K step counts below and above the ring depth, wide layers
-# with a ragged last workgroup (16, 32 and 64 weight rows per workgroup), the 8-wave form
-# (129-512 tokens, one or two rows of workgroups), and the tiled kernel where one round of
-# workgroups cannot cover the output (M = 513, or above 16384 outputs).
+# with a ragged last workgroup (16, 32, 64 and, up to 128 tokens above 16384 outputs, 128
+# weight rows per workgroup), the 8-wave form (129-512 tokens, one or two rows of
+# workgroups), and the tiled kernel where one round of workgroups cannot cover the output
+# (M = 513, 200 tokens on 20000 outputs, or 128 tokens above 32768).
 SKINNY_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (65, 100, 2048),
                 (128, 130, 1152), (129, 257, 256), (2, 18, 14336), (16, 9000, 256),
                 (32, 8200, 384), (64, 10000, 1152), (128, 8193, 640), (97, 8209, 128),
                 (111, 4097, 2176), (128, 14336, 384), (200, 4100, 640), (256, 9000, 1152),
                 (160, 6144, 512), (257, 300, 256), (100, 20000, 256), (400, 7000, 384),
+                (90, 16500, 384), (128, 32768, 256), (128, 32769, 128), (200, 20000, 256),
                 (513, 1000, 256)]
 
 
@@ -94,7 +96,7 @@ def test_fp8_few_tokens(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(256, 8193, 640), (2048, 4096, 1024), (512, 6144, 4096),
                                    (2048, 28672, 512), (128, 4096, 4096), (100, 14336, 1024),
                                    (256, 4096, 2048), (200, 14336, 512), (512, 4096, 1024),
-                                   (300, 4100, 512)])
+                                   (300, 4100, 512), (128, 28672, 1024)])
 def test_fp8_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
@@ -203,7 +205,7 @@ def test_int8_ragged(M, N, K):
 # MXFP4 one: repeated launches must give identical bits, equal to the oracle's.
 @pytest.mark.parametrize("M,N,K", [(2048, 4096, 1024), (512, 6144, 4096), (2048, 6144, 1024),
                                    (128, 4096, 4096), (100, 14336, 1024), (256, 4096, 2048),
-                                   (512, 4096, 1024)])
+                                   (512, 4096, 1024), (100, 24000, 512)])
 def test_int8_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, 3 * M + N + K)
