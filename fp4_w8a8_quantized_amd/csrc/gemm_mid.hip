@@ -1,4 +1,4 @@
-// W8A8 GEMM for 65-512 tokens on gfx950, the same result as the other GEMMs:
+// W8A8 GEMM for 33-512 tokens on gfx950, the same result as the other GEMMs:
 //   FP8   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )
 //   INT8  y = epilogue( fp32(fp32(acc_i32) s_x[m]) s_w[n] )
 // ("FP8 and FP4 inference, SmoothQuant and activation quantization", Scale granularity;

@@ -40,7 +40,7 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep);
 
-// 65-512 tokens: up to 256 token rows and 16-128 weight rows per workgroup of 4 or 8
+// 33-512 tokens: up to 256 token rows and 16-128 weight rows per workgroup of 4 or 8
 // waves; weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
 // Weight rows per workgroup of launch_gemm_mid for an M x N output (16, 32, 64, or 128 up
 // to 128 tokens), or 0 if even the widest would take more than one round of workgroups.
@@ -48,8 +48,8 @@ int mid_weight_rows(int64_t M, int64_t N);
 hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                            const Epilogue& ep);
-// Up to 64 tokens: weights streamed by 16-, 32- or 64-row workgroups that split K among
-// their waves.
+// Up to 32 tokens (64 on layers too wide for one round of the 33-512-token kernel):
+// weights streamed by 16-, 32- or 64-row workgroups that split K among their waves.
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                               const Epilogue& ep);

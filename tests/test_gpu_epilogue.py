@@ -25,7 +25,7 @@ TOL = 1e-2
 # 65-512-token kernel (4 and 8 waves, one and two rows of workgroups, narrow and wide)
 SHAPES = [(600, 549, 256), (256, 512, 384), (5, 130, 1152), (64, 10000, 256), (100, 262, 512),
           (128, 9001, 256), (200, 9001, 384), (300, 549, 256), (448, 2050, 256),
-          (300, 6100, 384), (100, 20001, 256)]
+          (300, 6100, 384), (100, 20001, 256), (48, 40000, 128), (40, 4100, 256)]
 
 
 def _inputs(M, N, K, seed):

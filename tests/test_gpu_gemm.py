@@ -66,7 +66,8 @@ def test_fp8_ragged(M, N, K):
     _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
 
 
-# Few-token paths (M <= 64: the weight-streaming kernel; 65 <= M <= 512: the kernel that
+# Few-token paths (M <= 32, and up to 64 above one round of the next kernel: the
+# weight-streaming kernel; 33 <= M <= 512: the kernel that
 # stages up to 256 token rows and 16-128 weight rows per workgroup): every 16-row bucket
 # edge, N not a multiple of 4 or 16, one K step (most waves idle; the weight ring then
 # re-fetches the only step), K step counts below and above the ring depth, wide layers
@@ -80,7 +81,7 @@ SKINNY_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (6
                 (111, 4097, 2176), (128, 14336, 384), (200, 4100, 640), (256, 9000, 1152),
                 (160, 6144, 512), (257, 300, 256), (100, 20000, 256), (400, 7000, 384),
                 (90, 16500, 384), (128, 32768, 256), (128, 32769, 128), (200, 20000, 256),
-                (513, 1000, 256)]
+                (513, 1000, 256), (40, 4100, 512), (64, 40000, 256), (48, 33000, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_CASES)
