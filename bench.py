@@ -72,7 +72,22 @@ def _parse_args():
                    help="write the traffic summary from four rocprofv3 counter_collection.csv files "
                         "(copy and prefill runs, FETCH_SIZE then WRITE_SIZE) and exit; no GPU needed")
     p.add_argument("--copy-mib", type=int, default=256, help="size used with --calibrate-copy")
+    p.add_argument("--mfma-summary", nargs=4, metavar=("OUT", "TITLE", "COMMAND", "CSV"),
+                   help="write a matrix-core utilisation summary from a rocprofv3 --pmc counter_collection.csv "
+                        "and exit; no GPU needed")
     return p.parse_args()
+
+
+QUANT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quantize_per_token_8b_traffic.txt")
+QUANT_SOURCES = [os.path.join(ROOT, "fp4_w8a8_quantized_amd", "csrc", f) for f in ("quantize.hip", "common.h")]
+
+
+def quant_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in QUANT_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def gemm_source_hash() -> str:
@@ -167,6 +182,104 @@ traffic_over_algorithmic = {(fetch + write) / alg:.3f}
         f.write(text)
     print(text)
 
+    # The per-token quantizer in the same runs: median over all of its dispatches (the
+    # timed steps, the passes over rotating X copies and the repeated pass on one X).
+    def quant_kib(path, tag):
+        v = [x for n, x in _counter_rows(path) if tag in n]
+        return float(np.median(v)), len(v)
+
+    qlines = []
+    for tag, K in (("quant_rows_kernel<2", 4096), ("quant_rows_kernel<7", 14336)):
+        qf, nqf = quant_kib(gf, tag)
+        qw, nqw = quant_kib(gw, tag)
+        fb, wb = qf * 1024.0 * f_scale, qw * 1024.0 * w_scale
+        M = 2048
+        qlines.append(f"# {tag}> (2048 x {K} bf16 -> E4M3FN): median of {nqf} / {nqw} dispatches\n"
+                      f"K{K}_algorithmic_read_bytes = {2 * M * K}\n"
+                      f"K{K}_algorithmic_write_bytes = {M * K + 4 * M}\n"
+                      f"K{K}_fetch_bytes_per_launch = {fb:.0f}\n"
+                      f"K{K}_write_bytes_per_launch = {wb:.0f}\n"
+                      f"K{K}_traffic_over_algorithmic = {(fb + wb) / (3 * M * K + 4 * M):.3f}\n")
+    qtext = (f"""# HBM traffic of the per-token E4M3FN quantizer (quant_rows_kernel) in the 8B prefill bench
+# commands: the four rocprofv3 --pmc runs listed in {os.path.basename(TRAFFIC_FILE)} (copy calibration and
+# the prefill bench under FETCH_SIZE, then WRITE_SIZE), then python3 bench.py --traffic-summary <the four csv>
+# copy calibration ({args.copy_mib} MiB each way): FETCH_SIZE scale {f_scale:.4f}, WRITE_SIZE scale {w_scale:.4f}
+quant_source_sha256_16 = {quant_source_hash()}
+""" + "".join(qlines))
+    with open(QUANT_TRAFFIC_FILE, "w") as f:
+        f.write(qtext)
+    print(qtext)
+
+
+def _counter_table(path):
+    """{dispatch id: (kernel name, duration s, {counter: value})} from a rocprofv3
+    counter_collection.csv (which carries each dispatch's start and end timestamps)."""
+    import csv
+    by = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            did = int(r.get("Dispatch_Id") or r.get("Dispatch-Id"))
+            name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+            ent = by.setdefault(did, (name, dur, {}))
+            ent[2][r.get("Counter_Name") or r.get("Counter-Name")] = float(
+                r.get("Counter_Value") or r.get("Counter-Value"))
+    return by
+
+
+# MI355X: 8 XCDs, 32 shader engines, 1024 SIMDs. SQ_VALU_MFMA_BUSY_CYCLES is summed over
+# the SIMDs, SQ_BUSY_CYCLES over the shader engines and GRBM_GUI_ACTIVE over the XCDs.
+N_XCD, N_SE, N_SIMD = 8, 32, 1024
+
+
+def mfma_summary(args):
+    """Per kernel: FLOPs from the MFMA op counters against 2MNK, the matrix cores' busy
+    cycles per SIMD, and the cycles the shader engines had waves, from one rocprofv3 --pmc
+    pass (SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE and the MOPS counters)."""
+    import numpy as np
+    out, title, cmd, path = args.mfma_summary
+    by = _counter_table(path)
+    groups = {}
+    for did, (name, dur, c) in sorted(by.items()):
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or c["SQ_VALU_MFMA_BUSY_CYCLES"] <= 0:
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "").replace("w8a8::", "")
+        flop = sum(c.get(k, 0.0) for k in ("SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_I8",
+                                            "SQ_INSTS_VALU_MFMA_MOPS_F6F4")) * 512
+        groups.setdefault((short, flop), []).append((dur, c))
+    lines = [f"# {title}",
+             "# command (from the repository root, on one MI355X; one --pmc pass in a run of its own):",
+             f"#   {cmd}",
+             f"#   python3 bench.py --mfma-summary <this file> <title> <command> <counter_collection.csv>",
+             "# Counters are summed over instances by rocprofv3: SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs,",
+             "# SQ_BUSY_CYCLES over the 32 shader engines, GRBM_GUI_ACTIVE over the 8 XCDs; MOPS counters count",
+             "# 512 flops (or int ops) each. Per dispatch, averaged over the dispatches of each kernel:",
+             "#   flop            = (SQ_INSTS_VALU_MFMA_MOPS_F8 + _I8 + _F6F4) * 512",
+             "#   mfma_busy       = SQ_VALU_MFMA_BUSY_CYCLES / 1024   (matrix-core busy cycles per SIMD)",
+             "#   se_busy         = SQ_BUSY_CYCLES / 32               (cycles with waves resident, per shader engine)",
+             "#   window          = GRBM_GUI_ACTIVE / 8               (counting window per XCD; it runs a few us past the kernel)",
+             "#   busy_of_active  = mfma_busy / se_busy               (matrix cores busy while the kernel's waves were resident)",
+             "#   mfma_util       = mfma_busy / window                (rocprofv3's MfmaUtil)",
+             "#   se_clock_GHz    = se_busy / duration                (a lower bound on the shader clock during the dispatch)",
+             "# Under --pmc every dispatch runs alone, between counter reads, so the clock is not the one of",
+             "# back-to-back launches; the bench's clock probe gives that one.",
+             "kernel | dispatches | mean_us | flop_per_dispatch | mfma_busy | se_busy | window | busy_of_active | mfma_util | se_clock_GHz"]
+    for (short, _), ds in sorted(groups.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        dur = np.array([d for d, _ in ds])
+        get = lambda k: np.array([c.get(k, 0.0) for _, c in ds])
+        flop = (get("SQ_INSTS_VALU_MFMA_MOPS_F8") + get("SQ_INSTS_VALU_MFMA_MOPS_I8")
+                + get("SQ_INSTS_VALU_MFMA_MOPS_F6F4")) * 512
+        busy = get("SQ_VALU_MFMA_BUSY_CYCLES") / N_SIMD
+        seb = get("SQ_BUSY_CYCLES") / N_SE
+        win = get("GRBM_GUI_ACTIVE") / N_XCD
+        lines.append(f"{short} | {len(ds)} | {dur.mean() * 1e6:.1f} | {flop.mean():.4e} | {busy.mean():.0f} | "
+                     f"{seb.mean():.0f} | {win.mean():.0f} | {np.mean(busy / np.maximum(seb, 1)):.3f} | "
+                     f"{np.mean(busy / np.maximum(win, 1)):.3f} | {np.mean(seb / dur) / 1e9:.3f}")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as f:
+        f.write(text)
+    print(text)
+
 
 def _threads() -> int:
     try:
@@ -205,6 +318,29 @@ def _base_record(args, metric, value, unit, ms_per_step, dtype, config, higher=T
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
             "higher_is_better": higher, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
             "data": "synthetic", "config": config}
+
+
+SPEC_SCLK_GHZ = 2.4           # the clock the MFMA peaks above are quoted at
+
+
+def sclk_during(c: Ctx, launch, n: int, window_ms: float = 15.0):
+    """Shader clock (GHz) the chip held while `launch(0) .. launch(n - 1)` ran back to back
+    on the bench stream: the library's clock probe runs on a second stream (one wave on one
+    CU of each XCD), enqueued behind the first launches so that its window falls inside the
+    run. Returns the median over the XCDs and the per-XCD figures."""
+    import numpy as np
+    torch = c.torch
+    out = torch.zeros((16,), dtype=torch.int64, device=c.dev)
+    side = torch.cuda.Stream(device=c.dev)
+    torch.cuda.synchronize()
+    for i in range(n):
+        launch(i)
+        if i == min(8, n - 1):
+            c.check(c.L.w8a8_sclk_probe(out.data_ptr(), 8, int(window_ms * 1e5), side.cuda_stream))
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().reshape(8, 2).astype(np.float64)
+    ghz = o[:, 1] / np.maximum(o[:, 0], 1) * 0.1
+    return float(np.median(ghz)), [round(float(g), 3) for g in ghz]
 
 
 def _launch_mean_s(c: Ctx, fn, reps: int) -> float:
@@ -342,7 +478,6 @@ def run_prefill(args, c: Ctx):
                 for _ in range(2 * max(10, math.ceil(600e6 / nb)))]
         cp_ms.append(timed_pass(lambda i, b=bufs: b[2 * i + 1].copy_(b[2 * i]), len(bufs) // 2))
         del bufs
-    del copies
     g_ms, q_ms, qc_ms, cp_ms = map(np.array, (g_ms, q_ms, qc_ms, cp_ms))
 
     # dominant kernel: the FP8 GEMM (algorithmic 2MNK per launch over its mean duration)
@@ -375,6 +510,20 @@ def run_prefill(args, c: Ctx):
     rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": FP8_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
                        "traffic": traffic}
+    # The shader clock over a run of the four GEMMs back to back (weights rotated as in the
+    # per-kernel passes) and over whole steps, from the clock probe on a second stream.
+    nrot = [len(w) for w in copies]
+    f_gemm, f_gemm_xcd = sclk_during(c, lambda i: gemm(dl[i % nl], copies[i % nl][(i // nl) % nrot[i % nl]]),
+                                     4 * nl * 16)
+    f_step, f_step_xcd = sclk_during(c, lambda i: (quant(dl[i % nl]), gemm(dl[i % nl], dl[i % nl]["wq"])),
+                                     4 * nl * 16)
+    rec["sclk"] = {"gemm_pass_GHz": round(f_gemm, 3), "step_GHz": round(f_step, 3),
+                   "gemm_pass_per_xcd_GHz": f_gemm_xcd, "step_per_xcd_GHz": f_step_xcd,
+                   "spec_GHz": SPEC_SCLK_GHZ,
+                   "method": "w8a8_sclk_probe on a second stream: shader cycles over 100 MHz "
+                             "real-time ticks, one wave per XCD, 15 ms window inside the run"}
+    rec["pct_of_peak_at_measured_clock"] = round(100.0 * value / (FP8_PEAK_TFLOPS * f_step / SPEC_SCLK_GHZ), 2)
+    rec["gemm_frac_at_measured_clock"] = round(achieved / (FP8_PEAK_TFLOPS * f_gemm / SPEC_SCLK_GHZ), 4)
     rec["kernels"] = {"gemm_fp8_mean_us": round(float(g_ms.mean()) * 1e3, 2),
                       "quantize_fp8_mean_us": round(float(q_ms.mean()) * 1e3, 2),
                       "quantize_fp8_GBps": round(q_gbps, 1),
@@ -384,6 +533,7 @@ def run_prefill(args, c: Ctx):
                       "quantize_over_copy": round(q_gbps / cp_gbps, 4),
                       "per_layer": per_layer,
                       "gemm_source_sha256_16": gemm_source_hash()}
+    del copies
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = prefill_cpu_baseline(layers, args.cpu_rows)
     return rec
@@ -757,6 +907,11 @@ def run_blockscaled(args, c: Ctx):
                                     "per 128-K group", "M": M, "K": K, "N": N})
     rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    f, f_xcd = sclk_during(c, lambda i: c.check(L.w8a8_gemm_blockscaled(
+        xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(), sh)),
+        8 + math.ceil(20e-3 / g_s))
+    rec["sclk"] = {"gemm_pass_GHz": round(f, 3), "gemm_pass_per_xcd_GHz": f_xcd, "spec_GHz": SPEC_SCLK_GHZ}
+    rec["gemm_frac_at_measured_clock"] = round(achieved / (FP8_PEAK_TFLOPS * f / SPEC_SCLK_GHZ), 4)
     q_bytes = 3.0 * M * K + 4.0 * M * (K // 128)
     rec["kernels"] = {"gemm_us": round(g_s * 1e6, 1), "group_quant_us": round(q_s * 1e6, 1),
                       "group_quant_GBps": round(q_bytes / q_s / 1e9, 1)}
@@ -803,6 +958,11 @@ def run_mxfp4(args, c: Ctx):
                        {"workload": "OCP MXFP4 operands (E2M1, E8M0 per 32 along K)", "M": M, "K": K, "N": N})
     rec["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP4_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(achieved / FP4_PEAK_TFLOPS, 4), "traffic": None}
+    f, f_xcd = sclk_during(c, lambda i: c.check(L.w8a8_gemm_mxfp4(
+        xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(), M, N, K, y.data_ptr(), sh)),
+        8 + math.ceil(20e-3 / g_s))
+    rec["sclk"] = {"gemm_pass_GHz": round(f, 3), "gemm_pass_per_xcd_GHz": f_xcd, "spec_GHz": SPEC_SCLK_GHZ}
+    rec["gemm_frac_at_measured_clock"] = round(achieved / (FP4_PEAK_TFLOPS * f / SPEC_SCLK_GHZ), 4)
     q_bytes = 2.5 * M * K + M * K / 32
     rec["kernels"] = {"gemm_us": round(g_s * 1e6, 1), "mx_quant_us": round(q_s * 1e6, 1),
                       "mx_quant_GBps": round(q_bytes / q_s / 1e9, 1)}
@@ -882,6 +1042,9 @@ def main():
 
     if args.traffic_summary:
         traffic_summary(args)
+        return
+    if args.mfma_summary:
+        mfma_summary(args)
         return
     import torch
     if not torch.cuda.is_available():

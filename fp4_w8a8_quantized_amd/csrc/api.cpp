@@ -268,4 +268,11 @@ w8a8_status w8a8_smooth_apply(const void* x_bf16, int64_t R, int64_t K, const fl
   return hip_status(w8a8::launch_smooth_apply(x_bf16, R, K, s, mode, out_bf16, as_stream(stream)));
 }
 
+w8a8_status w8a8_sclk_probe(uint64_t* out, int blocks, int64_t ticks, void* stream) {
+  if (blocks < 1 || blocks > 1024 || ticks < 1 || ticks > ((int64_t)1 << 32)) return W8A8_ERR_ARG;
+  if (!out) return W8A8_ERR_NULL;
+  if (!aligned16(out)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_sclk_probe(out, blocks, ticks, as_stream(stream)));
+}
+
 }  // extern "C"

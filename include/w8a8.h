@@ -292,6 +292,23 @@ w8a8_status w8a8_smoothquant_scales(const float* act_max, const float* w_max, in
 w8a8_status w8a8_smooth_apply(const void* x_bf16, int64_t R, int64_t K, const float* s,
                               int mode, void* out_bf16, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * Measurement helper (not part of the method): the shader clock a run actually held. The
+ * MFMA peak of a roofline is quoted at the 2.4 GHz maximum clock; the rate of the matrix
+ * cores is a fixed number of operations per shader cycle, so a kernel's fraction of the
+ * peak at the clock it ran at is its spec-peak fraction times 2.4 GHz / f.
+ *
+ * Launches `blocks` one-wave workgroups. Each reads the shader-cycle counter and the
+ * constant 100 MHz real-time counter at its start and again once `ticks` real-time ticks
+ * have passed, then writes out[2 b] = real-time ticks elapsed and out[2 b + 1] = shader
+ * cycles elapsed; f = out[2 b + 1] / out[2 b] * 100 MHz on workgroup b's XCD over that
+ * window. Enqueue it on a second stream just before the kernels to be measured; it takes
+ * one wave slot on `blocks` CUs.
+ *   out: uint64 [2 * blocks], 16-byte aligned device array.
+ *   1 <= blocks <= 1024 and 1 <= ticks <= 2^32 (W8A8_ERR_ARG otherwise).
+ */
+w8a8_status w8a8_sclk_probe(uint64_t* out, int blocks, int64_t ticks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

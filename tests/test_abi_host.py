@@ -206,3 +206,12 @@ def test_operand_byte_limit(L):
     assert L.w8a8_gemm_w4a16(A, A, A, lim // (2 * K) + 1, 4, K, A, None) == ESHAPE
     assert L.w8a8_quantize_per_token(A, lim // (2 * K) + 1, K, 0, A, A, None) == ESHAPE
     assert L.w8a8_quantize_int4(A, lim // (2 * K) + 1, K, A, A, None) == ESHAPE
+
+
+def test_sclk_probe_validation(L):
+    assert L.w8a8_sclk_probe(A, 0, 100, None) == EARG
+    assert L.w8a8_sclk_probe(A, 1025, 100, None) == EARG
+    assert L.w8a8_sclk_probe(A, 8, 0, None) == EARG
+    assert L.w8a8_sclk_probe(A, 8, (1 << 32) + 1, None) == EARG
+    assert L.w8a8_sclk_probe(None, 8, 100, None) == ENULL
+    assert L.w8a8_sclk_probe(A + 8, 8, 100, None) == EALIGN
