@@ -6,14 +6,17 @@
 // activation quantization", Scale granularity; "FP8 and INT8 Inference" §6-9, the GEMM
 // epilogue; "Low-bit LLM Weights and Activations" §3.4).
 //
-// Up to 32 tokens (the weights dominate the traffic): the weight-streaming kernel of
-// gemm_skinny.hip. 33-512 tokens, where one round of workgroups covers the output:
-// gemm_mid.hip, whose workgroups hold up to 256 token rows against 16-128 weight rows (a
-// 256-row tile would leave most CUs idle on 4096-wide layers; measured faster than the
-// weight-streaming kernel from 48 tokens, slower at 32). Up to 64 tokens on wider layers,
-// the weight-streaming kernel again. Otherwise the
-// two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8 on 32x32x32
-// MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
+// Dispatch by shape:
+//  - narrow tiles sized to the token count (gemm_narrow.hip) where they measured faster: up
+//    to 64 tokens on layers wider than 4096 outputs, 65-128 tokens above 8192 outputs, and
+//    256-512 tokens where one round of 128 x 64 tiles covers the output;
+//  - otherwise up to 32 tokens (the weights dominate the traffic): the weight-streaming
+//    kernel of gemm_skinny.hip;
+//  - 33-512 tokens, where one round of workgroups covers the output: gemm_mid.hip, whose
+//    workgroups hold up to 256 token rows against 16-128 weight rows (a 256-row tile would
+//    leave most CUs idle on 4096-wide layers);
+//  - otherwise the two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8
+//    on 32x32x32 MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
 #include "common.h"
 #include "internal.h"
 
@@ -22,10 +25,10 @@ namespace w8a8 {
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                        const Epilogue& ep) {
+  if (use_gemm_narrow(M, N, K)) return launch_gemm_narrow(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (M <= 32) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (M <= 512 && mid_weight_rows(M, N) != 0)
     return launch_gemm_mid(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
-  if (M <= 64) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
   return launch_gemm_int8_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
 }

@@ -87,23 +87,13 @@ hipError_t launch_smooth_scales(const float* a, const float* w, int64_t K, float
 hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float* s, int mode,
                                void* out, hipStream_t st);
 
-// Split-K GEMM for few and mid-size token counts: BM x BN output tiles (BM 16-128 token
-// rows, BN 64 or 128 weight rows), the K steps of each tile split over `splits`
-// workgroups whose fp32 / INT32 partials meet in a workspace; the last workgroup of a tile
-// to finish adds them in split order and applies the epilogue.
-struct SplitKConfig {
-  int bm = 16, bn = 64, splits = 1;
-  int64_t tiles = 0;
-};
-SplitKConfig splitk_config(int64_t M, int64_t N, int64_t K);
-// Workspace of a configuration: a zero-initialised uint32 counter per tile (rounded up to
-// 256 bytes; every call leaves them zero again), then splits x tiles partial tiles of
-// BM x BN x 4 bytes. 0 when splits == 1 (no workspace is read or written).
-int64_t splitk_workspace_bytes(const SplitKConfig& c);
-int64_t splitk_counter_bytes(const SplitKConfig& c);
-hipError_t launch_gemm_splitk(const SplitKConfig& c, const void* xq, const float* sx, const void* wq,
-                              const float* sw, int64_t M, int64_t N, int64_t K, int fmt, void* y,
-                              hipStream_t st, const Epilogue& ep, void* workspace);
+// Narrow output tiles sized to the token count (16-128 token rows x 64 or 128 weight rows,
+// 4 waves, K steps through an LDS ring): where it measured faster than the other few-token
+// and mid-size kernels (use_gemm_narrow).
+bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_narrow(const void* xq, const float* sx, const void* wq, const float* sw,
+                              int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
+                              const Epilogue& ep);
 
 // Measurement: one-wave workgroups that record real-time ticks and shader cycles over a
 // window of `ticks` real-time ticks (100 MHz).
