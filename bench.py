@@ -60,8 +60,8 @@ def _parse_args():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill",
-                   choices=["prefill", "msweep", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16", "epilogue",
-                            "static", "all"])
+                   choices=["prefill", "msweep", "qsweep", "decode", "blockscaled", "mxfp4", "nvfp4", "w4a16",
+                            "epilogue", "static", "all"])
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     p.add_argument("--cpu-rows", type=int, default=2048,
                    help="tokens per linear in the prefill oracle sample (rows are independent)")
@@ -445,9 +445,10 @@ def run_prefill(args, c: Ctx):
     # The GEMMs rotate over copies of the weights and the quantizer over copies of X (each
     # >600 MB per layer), so that every launch reads its operands from HBM as in the step,
     # where the weight stream pushes X out of the 256 MB last-level cache. A third pass
-    # repeats the quantizer on one X, which then stays in that cache, and a fourth times a
-    # plain device copy of the quantizer's bytes (1.5 B read and 1.5 B written per element of
-    # X, against its 2 + 1) over rotating buffers: what HBM gives at these sizes.
+    # repeats the quantizer on one X, which then stays in that cache, and a fourth runs the
+    # library's same-split stream kernel (2 bytes read, 1 written per element, like the
+    # quantizer, with no arithmetic) over the same rotating X copies: what HBM gives an
+    # elementwise codec at these sizes.
     def spacer():
         for _ in range(2):
             for d in dl:
@@ -473,11 +474,11 @@ def run_prefill(args, c: Ctx):
         q_ms.append(timed_pass(lambda i, d=d, xc=xc: quant(d, xc[i]), len(xc)))
         del xc
         qc_ms.append(timed_pass(lambda i, d=d: quant(d), reps))
-        nb = (3 * d["M"] * d["K"]) // 2
-        bufs = [torch.empty((nb,), dtype=torch.uint8, device=c.dev)
-                for _ in range(2 * max(10, math.ceil(600e6 / nb)))]
-        cp_ms.append(timed_pass(lambda i, b=bufs: b[2 * i + 1].copy_(b[2 * i]), len(bufs) // 2))
-        del bufs
+        xc = [d["x"]] + [d["x"].clone() for _ in range(max(reps, math.ceil(600e6 / d["x"].nbytes)) - 1)]
+        n = d["M"] * d["K"]
+        cp_ms.append(timed_pass(lambda i, d=d, xc=xc, n=n: c.check(L.w8a8_stream_probe(
+            xc[i % len(xc)].data_ptr(), n, d["xq"].data_ptr(), sh)), len(xc)))
+        del xc
     g_ms, q_ms, qc_ms, cp_ms = map(np.array, (g_ms, q_ms, qc_ms, cp_ms))
 
     # dominant kernel: the FP8 GEMM (algorithmic 2MNK per launch over its mean duration)
@@ -496,7 +497,7 @@ def run_prefill(args, c: Ctx):
                              "quant_us": round(q_ms[i] * 1e3, 2),
                              "quant_GBps": round(q_bytes[i] / (q_ms[i] * 1e-3) / 1e9, 1),
                              "quant_cached_us": round(qc_ms[i] * 1e3, 2),
-                             "copy_same_bytes_us": round(cp_ms[i] * 1e3, 2)}
+                             "stream_same_split_us": round(cp_ms[i] * 1e3, 2)}
                  for i, d in enumerate(dl)}
 
     rec = _base_record(
@@ -529,8 +530,8 @@ def run_prefill(args, c: Ctx):
                       "quantize_fp8_GBps": round(q_gbps, 1),
                       "quantize_fp8_hbm_frac": round(q_gbps / HBM_PEAK_GBPS, 4),
                       "quantize_fp8_cached_GBps": round(qc_gbps, 1),
-                      "copy_same_bytes_GBps": round(cp_gbps, 1),
-                      "quantize_over_copy": round(q_gbps / cp_gbps, 4),
+                      "stream_same_split_GBps": round(cp_gbps, 1),
+                      "quantize_over_stream": round(q_gbps / cp_gbps, 4),
                       "per_layer": per_layer,
                       "gemm_source_sha256_16": gemm_source_hash()}
     del copies
@@ -594,6 +595,69 @@ def run_msweep(args, c: Ctx):
     rec["roofline"] = {"bound": "mfma", "achieved": round(value, 1), "peak": FP8_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": round(value / FP8_PEAK_TFLOPS, 4), "traffic": None}
     rec["sweep"] = per_m
+    return rec
+
+
+# ----------------------------------------------------------------------------- quantizer sweep
+QSWEEP_M = (2048, 4096, 8192, 16384)
+QSWEEP_K = (4096, 14336)
+
+
+def run_qsweep(args, c: Ctx):
+    """The per-token E4M3FN quantizer (and the static per-tensor one) against the
+    same-split stream kernel (2 bytes read, 1 byte written per element, the quantizers'
+    traffic) at M in {2048 .. 16384} tokens, K in {4096, 14336}: X rotated over copies of at
+    least 600 MB, so that every launch reads it from HBM. Inputs: N(0,1) with 0.1% of the
+    channels scaled by 50-500, drawn on the device from a seeded generator."""
+    torch, L, sh = c.torch, c.L, c.sh
+    rows = []
+    for K in QSWEEP_K:
+        for M in QSWEEP_M:
+            gen = torch.Generator(device=c.dev)
+            gen.manual_seed(7000 + M + K)
+            n = M * K
+            copies = max(2, math.ceil(600e6 / (2 * n)))
+            ch = torch.randperm(K, generator=gen, device=c.dev)[:max(1, round(0.001 * K))]
+            fac = 50.0 * torch.exp(torch.rand(len(ch), generator=gen, device=c.dev) * math.log(10.0))
+            xs = []
+            for _ in range(copies):
+                x = torch.randn((M, K), generator=gen, device=c.dev)
+                x[:, ch] *= fac
+                xs.append(x.to(torch.bfloat16))
+                del x
+            q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=c.dev)
+            sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
+            scale = torch.tensor([float(xs[0].float().abs().max()) / 448.0], dtype=torch.float32, device=c.dev)
+            sat = torch.zeros((1,), dtype=torch.int32, device=c.dev)
+            amax = torch.zeros((1,), dtype=torch.float32, device=c.dev)
+            reps = 3 * copies
+            for i in range(2 * copies):                      # untimed: clocks and caches settle
+                c.check(L.w8a8_quantize_per_token(xs[i % copies].data_ptr(), M, K, 0, q.data_ptr(),
+                                                  sx.data_ptr(), sh))
+            dyn = _launch_mean_s(c, lambda i: c.check(L.w8a8_quantize_per_token(
+                xs[i % copies].data_ptr(), M, K, 0, q.data_ptr(), sx.data_ptr(), sh)), reps)
+            sta = _launch_mean_s(c, lambda i: c.check(L.w8a8_quantize_static(
+                xs[i % copies].data_ptr(), M, K, 0, scale.data_ptr(), q.data_ptr(), sat.data_ptr(),
+                amax.data_ptr(), sh)), reps)
+            stream = _launch_mean_s(c, lambda i: c.check(L.w8a8_stream_probe(
+                xs[i % copies].data_ptr(), n, q.data_ptr(), sh)), reps)
+            byt = 3.0 * n
+            rows.append({"M": M, "K": K, "bytes": int(byt + 4 * M),
+                         "dynamic_us": round(dyn * 1e6, 2), "dynamic_GBps": round((byt + 4 * M) / dyn / 1e9, 1),
+                         "dynamic_hbm_frac": round((byt + 4 * M) / dyn / 1e9 / HBM_PEAK_GBPS, 4),
+                         "static_us": round(sta * 1e6, 2), "static_GBps": round(byt / sta / 1e9, 1),
+                         "stream_us": round(stream * 1e6, 2), "stream_GBps": round(byt / stream / 1e9, 1),
+                         "dynamic_over_stream": round(stream / dyn, 4)})
+            del xs, q
+            torch.cuda.empty_cache()
+    top = rows[-1]
+    rec = _base_record(args, "Per-token E4M3FN quantize HBM GB/s vs tokens (largest M, K=14336)",
+                       top["dynamic_GBps"], "GB/s", top["dynamic_us"] / 1e3, "bf16->fp8_e4m3fn",
+                       {"workload": "per-token dynamic E4M3FN quantization of bf16 X, M in {2048, 4096, 8192, "
+                                    "16384} tokens, K in {4096, 14336}; X rotated over >600 MB of copies"})
+    rec["roofline"] = {"bound": "hbm", "achieved": top["dynamic_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": top["dynamic_hbm_frac"], "traffic": None}
+    rec["sweep"] = rows
     return rec
 
 
@@ -1060,7 +1124,8 @@ def main():
         print(json.dumps({"calibration_copy_bytes": n}), flush=True)
         return
     c = Ctx()
-    runs = {"prefill": run_prefill, "msweep": run_msweep, "decode": run_decode, "blockscaled": run_blockscaled,
+    runs = {"prefill": run_prefill, "msweep": run_msweep, "qsweep": run_qsweep, "decode": run_decode,
+            "blockscaled": run_blockscaled,
             "epilogue": run_epilogue, "static": run_static,
             "mxfp4": run_mxfp4, "nvfp4": run_nvfp4, "w4a16": run_w4a16}
     names = list(runs) if args.workload == "all" else [args.workload]

@@ -61,6 +61,7 @@ _SIGNATURES = {
     "w8a8_smoothquant_scales": [_c_vp, _c_vp, _c_i64, _c_float, _c_vp, _c_vp],
     "w8a8_smooth_apply": [_c_vp, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_vp],
     "w8a8_sclk_probe": [_c_vp, _c_int, _c_i64, _c_vp],
+    "w8a8_stream_probe": [_c_vp, _c_i64, _c_vp, _c_vp],
 }
 
 _lib = None

@@ -275,4 +275,13 @@ w8a8_status w8a8_sclk_probe(uint64_t* out, int blocks, int64_t ticks, void* stre
   return hip_status(w8a8::launch_sclk_probe(out, blocks, ticks, as_stream(stream)));
 }
 
+w8a8_status w8a8_stream_probe(const void* x_bf16, int64_t n, void* y, void* stream) {
+  if (n < 0 || n > kMaxOperandBytes / 2) return W8A8_ERR_SHAPE;
+  if (n % 8 != 0) return W8A8_ERR_UNSUPPORTED;
+  if (n == 0) return W8A8_OK;
+  if (!x_bf16 || !y) return W8A8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(y)) return W8A8_ERR_ALIGN;
+  return hip_status(w8a8::launch_stream_probe(x_bf16, n, y, as_stream(stream)));
+}
+
 }  // extern "C"

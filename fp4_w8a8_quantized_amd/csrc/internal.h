@@ -98,5 +98,7 @@ hipError_t launch_gemm_narrow(const void* xq, const float* sx, const void* wq, c
 // Measurement: one-wave workgroups that record real-time ticks and shader cycles over a
 // window of `ticks` real-time ticks (100 MHz).
 hipError_t launch_sclk_probe(uint64_t* out, int blocks, int64_t ticks, hipStream_t st);
+// Measurement: read n bf16 values and write one byte each (the quantizers' traffic split).
+hipError_t launch_stream_probe(const void* x, int64_t n, void* y, hipStream_t st);
 
 }  // namespace w8a8

@@ -17,6 +17,15 @@
 // number; for s in [2^-60, 2^60] every quotient that can change a code (|x / s| >= 2^-11)
 // is one. Other scales divide per element. Counter and maximum are reduced per block and reach memory
 // through at most one vector-memory atomic each per block.
+//
+// Layout of the work: each thread encodes four 16-byte chunks whose loads are all issued
+// first, one block per 1024 chunks (measured on 2048 x 4096 and up: within 1-9% of the
+// per-token quantizer when nothing saturates). Variants that did worse: a grid capped at
+// 1024 blocks looping over one chunk per thread (2.5 against 2.9 TB/s), a grid capped at
+// 512 blocks prefetching its next tile, 1024-thread blocks, eight chunks per thread, and an
+// unconditional atomic maximum per block (20 us instead of 6 on 2048 x 4096: atomics on one
+// address serialize). When every block saturates, its count atomic costs about 2 us per
+// call at 2048 x 4096.
 #include <type_traits>
 
 #include "common.h"
@@ -38,13 +47,21 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const u32x4* __restri
   const bool shortcut = s >= 0x1p-60f && s <= 0x1p60f;
   uint32_t sat = 0;
   float amax = 0.0f;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // Thread t of block b owns the chunks b * 1024 + t + 256 i, i < 4: all four loads are
+  // issued before the first is encoded, so each thread keeps 64 bytes in flight.
+  const int64_t c0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = (c0 + 256 * i < nchunks) ? __builtin_nontemporal_load(x + c0 + 256 * i) : u32x4{0u, 0u, 0u, 0u};
   auto run = [&](auto fast) {
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < nchunks; c += stride) {
-      const u32x4 v = __builtin_nontemporal_load(x + c);
-      amax = fmaxf(amax, chunk_absmax(v));
-      float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t c = c0 + 256 * i;
+      if (c >= nchunks) break;
+      amax = fmaxf(amax, chunk_absmax(v[i]));
+      float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                    bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = decltype(fast)::value ? div_static(f[e], s, rcp) : f[e] / s;
       u32x2 o;
@@ -117,8 +134,7 @@ __global__ __launch_bounds__(256) void delayed_scale_kernel(float* __restrict__ 
 hipError_t launch_quantize_static(const void* x, int64_t M, int64_t K, int fmt, const float* scale,
                                   void* q, uint32_t* saturated, float* amax, hipStream_t st) {
   const int64_t nchunks = M * K / 8;
-  const int64_t want = (nchunks + 255) / 256;
-  const int blocks = (int)(want < 1024 ? want : 1024);
+  const int blocks = (int)((nchunks + 1023) / 1024);   // 4 chunks per thread, 256 threads
   if (fmt == 1)
     hipLaunchKernelGGL(quant_static_kernel<true>, dim3(blocks), dim3(256), 0, st,
                        (const u32x4*)x, nchunks, scale, (u32x2*)q, saturated, amax);

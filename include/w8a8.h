@@ -309,6 +309,14 @@ w8a8_status w8a8_smooth_apply(const void* x_bf16, int64_t R, int64_t K, const fl
  */
 w8a8_status w8a8_sclk_probe(uint64_t* out, int blocks, int64_t ticks, void* stream);
 
+/* Measurement helper (not part of the method): the HBM ceiling of the quantizers' traffic.
+ * Reads n bf16 values of x_bf16 and writes one byte per value to y (the high byte of the
+ * bf16), the 2-bytes-in, 1-byte-out split of the per-token and static quantizers, with no
+ * arithmetic to speak of; each thread keeps four 16-byte loads in flight.
+ *   x_bf16: [n] bf16, y: [n] bytes, both 16-byte aligned device arrays; n % 8 == 0
+ *   (W8A8_ERR_UNSUPPORTED), 0 <= n <= 2^30 (W8A8_ERR_SHAPE). */
+w8a8_status w8a8_stream_probe(const void* x_bf16, int64_t n, void* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -215,3 +215,11 @@ def test_sclk_probe_validation(L):
     assert L.w8a8_sclk_probe(A, 8, (1 << 32) + 1, None) == EARG
     assert L.w8a8_sclk_probe(None, 8, 100, None) == ENULL
     assert L.w8a8_sclk_probe(A + 8, 8, 100, None) == EALIGN
+
+
+def test_stream_probe_validation(L):
+    assert L.w8a8_stream_probe(A, -8, A, None) == ESHAPE
+    assert L.w8a8_stream_probe(A, 12, A, None) == EUNSUP
+    assert L.w8a8_stream_probe(None, 16, A, None) == ENULL
+    assert L.w8a8_stream_probe(A, 16, A + 4, None) == EALIGN
+    assert L.w8a8_stream_probe(A, 0, None, None) == 0

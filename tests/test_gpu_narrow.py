@@ -120,3 +120,17 @@ def test_sclk_probe_reads_a_plausible_clock():
     assert np.all(o[:, 0] >= 200000) and np.all(o[:, 0] < 400000), o
     ghz = o[:, 1] / o[:, 0] * 0.1
     assert np.all(ghz > 0.1) and np.all(ghz < 2.5), ghz
+
+
+def test_stream_probe_writes_the_high_bytes():
+    """The same-split stream kernel the quantizer is measured against: output byte i is the
+    high byte of bf16 element i, over a ragged count of 16-byte chunks."""
+    need_gpu()
+    rng = np.random.default_rng(3)
+    n = 8 * 12345
+    bits = rng.integers(0, 65536, size=n, dtype=np.uint16)
+    x = torch.from_numpy(bits.view(np.int16)).to("cuda:0")
+    y = torch.zeros((n,), dtype=torch.uint8, device="cuda:0")
+    assert w8.lib().w8a8_stream_probe(x.data_ptr(), n, y.data_ptr(), torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), (bits >> 8).astype(np.uint8))
