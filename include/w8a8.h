@@ -277,8 +277,9 @@ w8a8_status w8a8_gemm_w4a16(const void* x_bf16, const void* q_packed, const uint
 w8a8_status w8a8_channel_absmax(const void* x_bf16, int64_t R, int64_t K, float* amax,
                                 void* stream);
 
-/* Smoothing factors s[j] = max(act_max[j], 1e-5)^alpha / max(w_max[j], 1e-5)^(1-alpha),
- * evaluated in fp32. alpha = 0.5 uses correctly rounded square roots and one correctly
+/* Smoothing factors s[j] = max(act_max[j], 1e-5)^alpha / max(w_max[j], 1e-5)^(1-alpha)
+ * ([P-LOWBIT] §4.3, the migration strength alpha; [P-FP8FP4] `smooth`), evaluated in fp32
+ * on the device, so that the maxima from w8a8_channel_absmax never go through the host. alpha = 0.5 uses correctly rounded square roots and one correctly
  * rounded division (a fully specified fp32 result); alpha = 0 and 1 reduce to 1/w and a;
  * other alpha in (0, 1) use exp2/log2 and are accurate to a few ulp.
  *   act_max, w_max, s: fp32 [K] device arrays.    0 <= alpha <= 1 (W8A8_ERR_ARG). */

@@ -355,6 +355,21 @@ def test_mxfp4_ragged(M, N, K):
     _mx_compare(xb, wb, f"{M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 130, 512), (300, 549, 1024), (513, 384, 2048)])
+def test_mxfp4_scales_span_binades(M, N, K):
+    """Every (row, 32-element block) of both operands at its own power of two in
+    2^-12 .. 2^12, so that the E8M0 scales of W vary as much as those of X: applying a
+    neighbouring row's or block's scale in the scaled MFMA moves the output by orders of
+    magnitude. Ragged and multi-tile shapes."""
+    need_gpu()
+    rng = np.random.default_rng(M + 5 * N + K)
+    xs = np.exp2(rng.integers(-12, 13, size=(M, K // 32))).repeat(32, axis=1)
+    ws = np.exp2(rng.integers(-12, 13, size=(N, K // 32))).repeat(32, axis=1)
+    xb = _bf16(rng.standard_normal((M, K)) * xs)
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02 * ws)
+    _mx_compare(xb, wb, f"binade-scaled mxfp4 {M}x{N}x{K}")
+
+
 def test_mxfp4_full_size_sampled():
     need_gpu()
     xb, wb = synthetic.mxfp4()

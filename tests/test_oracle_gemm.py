@@ -82,6 +82,36 @@ def test_int8_acc_exact_and_epilogue_order():
             assert y[m, n] == F.f64_to_bf16_rne(np.array([float(v)]))[0]
 
 
+def test_int8_epilogue_rounding_order_hand_case():
+    """A hand case where the order of the INT8 epilogue's roundings shows in the bf16
+    output ("FP8 and INT8 Inference" §5 writes Y_int32 x s_x x s_w, left to right). With
+    acc = -13999889 (exact in fp32), s_x = 0x3B201C75 and s_w = 0x3A8B6513 (bit patterns of
+    fp32 scales): each product of a 24-bit integer or significand and a 24-bit significand
+    is exact in fp64, so the roundings below are exactly the ones they name.
+      left to right:  t = fp32(acc s_x), v = fp32(t s_w)      -> bf16 0xC212
+      scales first:   v = fp32(acc fp32(s_x s_w))             -> bf16 0xC211
+      one rounding:   v = fp32(acc s_x s_w)                   -> bf16 0xC211
+    The oracle must give the left-to-right result; a dropped intermediate rounding or a
+    product of the two scales taken first fails here."""
+    acc = -13999889
+    sx = np.array([0x3B201C75], np.uint32).view(np.float32)[0]
+    sw = np.array([0x3A8B6513], np.uint32).view(np.float32)[0]
+
+    def bf16_rne(v32):
+        u = int(np.float32(v32).view(np.uint32))
+        return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) & 0xFFFF
+
+    t = np.float32(float(acc) * float(sx))                       # exact fp64 product, one rounding
+    left_to_right = bf16_rne(np.float32(float(t) * float(sw)))
+    scales_first = bf16_rne(np.float32(float(acc) * float(np.float32(float(sx) * float(sw)))))
+    from fractions import Fraction
+    exact = Fraction(acc) * Fraction(float(sx)) * Fraction(float(sw))
+    one_rounding = bf16_rne(np.float32(float(exact)))            # exact < 2^53 ulps: float() is RNE
+    assert (left_to_right, scales_first, one_rounding) == (0xC212, 0xC211, 0xC211)
+    y = G.int8_epilogue_bf16(np.array([[acc]], np.int64), np.array([sx]), np.array([sw]))
+    assert int(y[0, 0]) == 0xC212
+
+
 def test_smoothquant_worked_example_product():
     """The printed 2x2 product of the smoothed 4-bit example: the activation codes come
     from the printed quantized activations; an exhaustive search over all 4-bit weight
