@@ -51,7 +51,7 @@ HBM_PEAK_GBPS = 8000.0        # MI355X HBM3E
 FP16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16 / bf16 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp8_gemm_prefill_8b_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "fp4_w8a8_quantized_amd", "csrc", f)
-                for f in ("gemm_pp.hip", "common.h")]
+                for f in ("gemm_pp.hip", "gemm_solo.hip", "common.h")]
 
 
 def _parse_args():
@@ -151,7 +151,7 @@ def traffic_summary(args):
 
     def gemm_kib(path):
         nl = len(synthetic.PREFILL_SHAPES)
-        v = [x for n, x in _counter_rows(path) if "gemm_pp_kernel" in n]
+        v = [x for n, x in _counter_rows(path) if "gemm_pp_kernel" in n or "gemm_solo_kernel" in n]
         v = v[nl * TRAFFIC_WARMUP: nl * (TRAFFIC_WARMUP + TRAFFIC_STEPS)]   # the timed steps
         return float(np.mean(v)), len(v)
 

@@ -422,6 +422,12 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
   auto cost = [&](int64_t bn, int64_t per_tile) { return ((tm * ((N + bn - 1) / bn) + 255) / 256) * per_tile; };
   const int64_t c224 = cost(224, 270), c192 = cost(192, 240), c128 = cost(128, 194);
   const int bn = (c224 < c192 && c224 < c128) ? 224 : (c192 <= c128 ? 192 : 128);
+  // 128-wide tiles in up to two rounds over the CUs: the one-wave-per-SIMD kernel, which
+  // reads a quarter fewer fragment bytes per MFMA (2048 x 4096 x 4096: 34.7 -> 32.6 us;
+  // 2048 x 4096 x 14336: 102.5 -> 93.4 us; 4096 x 4096 x 4096: 64.7 -> 62.1 us). At four
+  // rounds (8192 x 4096 x 14336) it measured 3% slower.
+  if (bn == 128 && tm * ((N + 127) / 128) <= 512)
+    return launch_gemm_solo(xq, sx, wq, sw, M, N, K, y, st, ep);
   if (ep.out_fp8) {
     if (bn == 224) return launch_pp<224, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
     return bn == 192 ? launch_pp<192, true>(xq, sx, wq, sw, M, N, K, y, st, ep)

@@ -40,6 +40,12 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
                           int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                           const Epilogue& ep);
 
+// FP8 256 x 128 tiles on one wave per SIMD (128 x 64 wave tiles, fragments double-buffered,
+// one barrier per K step).
+hipError_t launch_gemm_solo(const void* xq, const float* sx, const void* wq, const float* sw,
+                            int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                            const Epilogue& ep);
+
 // 33-512 tokens: up to 256 token rows and 16-128 weight rows per workgroup of 4 or 8
 // waves; weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
 // Weight rows per workgroup of launch_gemm_mid for an M x N output (16, 32, 64, or 128 up
