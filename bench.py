@@ -577,8 +577,10 @@ def run_msweep(args, c: Ctx):
                 gemm(w)
             g = _launch_mean_s(c, lambda i, ws=ws: gemm(ws[i]), len(ws))
             pair = _launch_mean_s(c, lambda i, ws=ws: (quant(), gemm(ws[i])), len(ws))
+            f_ghz, _ = sclk_during(c, lambda i, ws=ws: gemm(ws[i % len(ws)]), 8 + math.ceil(20e-3 / g))
             f = 2.0 * M * N * K
-            layers.append({"layer": name, "N": N, "K": K, "gemm_us": round(g * 1e6, 1),
+            layers.append({"layer": name, "N": N, "K": K, "gemm_us": round(g * 1e6, 1), "sclk_GHz": round(f_ghz, 3),
+                           "gemm_frac_at_measured_clock": round(2.0 * M * N * K / g / 1e12 / (FP8_PEAK_TFLOPS * f_ghz / SPEC_SCLK_GHZ), 4),
                            "gemm_tflops": round(f / g / 1e12, 1), "quant_gemm_us": round(pair * 1e6, 1)})
             flops, g_s, pair_s = flops + f, g_s + g, pair_s + pair
             del ws, x, xq, y
