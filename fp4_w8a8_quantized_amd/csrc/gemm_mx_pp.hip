@@ -400,8 +400,13 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 
 }  // namespace
 
+// MXFP4: 256 x 256 tiles on one wave per SIMD (gemm_mx_solo.hip) once they fill a round of
+// the CUs (8192^3: 365 -> 293 us; 4096^3: 52 -> 42 us; 4096 x 18432 x 7168: 364 -> 316 us);
+// below that the 256 x 128 tiles of this kernel (2048 x 4096 x 4096: 27 against 37 us).
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq, const uint8_t* sw,
                              int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
+  if (((M + 255) / 256) * ((N + 255) / 256) >= 256)
+    return launch_gemm_mx_solo(xq, sx, wq, sw, M, N, K, y, st);
   const int tiles_m = (int)((M + kMxBM - 1) / kMxBM);
   const int tiles_n = (int)((N + kMxBN - 1) / kMxBN);
   hipLaunchKernelGGL((gemm_mx_pp_kernel<false, false, kMxBN>), dim3((unsigned)(tiles_m * tiles_n)),

@@ -82,6 +82,9 @@ hipError_t launch_gemm_w4a16_mid(const void* x, const void* wq, const uint16_t* 
 hipError_t launch_gemm_int8_pp(const void* xq, const float* sx, const void* wq, const float* sw,
                                int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                                const Epilogue& ep);
+// MXFP4 on 256 x 256 tiles, one wave per SIMD (128 x 128 wave tiles, accumulators in AGPRs).
+hipError_t launch_gemm_mx_solo(const void* xq, const uint8_t* sx, const void* wq, const uint8_t* sw,
+                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq,
                              const uint8_t* sw, int64_t M, int64_t N, int64_t K, void* y,
                              hipStream_t st);

@@ -370,6 +370,49 @@ def test_mxfp4_scales_span_binades(M, N, K):
     _mx_compare(xb, wb, f"binade-scaled mxfp4 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,binades", [(4097, 4100, 512, False), (4096, 4352, 768, True),
+                                            (4352, 4096, 256, True)])
+def test_mxfp4_wide_tiles(M, N, K, binades):
+    """Shapes with at least one round of 256 x 256 tiles, which the one-wave-per-SIMD MXFP4
+    kernel takes: ragged M and N, one to three K steps, scales of both operands at their
+    own powers of two per (row, 32-block); sampled rows and columns that include every tile
+    edge at both ends."""
+    need_gpu()
+    rng = np.random.default_rng(M + 3 * N + K)
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((N, K)) * 0.02
+    if binades:
+        x *= np.exp2(rng.integers(-12, 13, size=(M, K // 32))).repeat(32, axis=1)
+        w *= np.exp2(rng.integers(-12, 13, size=(N, K // 32))).repeat(32, axis=1)
+    xb, wb = _bf16(x), _bf16(w)
+    edges = lambda n: np.unique(np.clip(np.concatenate([np.arange(0, n, 256), np.arange(255, n, 256), [n - 1]]), 0, n - 1))
+    rows = np.unique(np.concatenate([edges(M), rng.choice(M, 40, replace=False)]))
+    cols = np.unique(np.concatenate([edges(N), rng.choice(N, 40, replace=False)]))
+    _mx_compare(xb, wb, f"mxfp4 wide tiles {M}x{N}x{K}", rows=rows, cols=cols)
+
+
+def test_mxfp4_wide_tiles_repeat_identical():
+    """The one-wave-per-SIMD MXFP4 kernel refills a stage while waves still compute on
+    fragments read from the other; repeated launches must give identical bits."""
+    need_gpu()
+    rng = np.random.default_rng(77)
+    xb = synthetic.mxfp4_x(4096, 1024)
+    wb = _bf16(rng.standard_normal((4096, 1024)) * 0.02)
+    xq, sx = w8.quantize_mxfp4(to_dev_bf16(xb))
+    wq, sw = w8.quantize_mxfp4(to_dev_bf16(wb))
+    y0 = w8.gemm_mxfp4(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    ref = y0.clone()
+    for r in range(10):
+        w8.gemm_mxfp4(xq, sx, wq, sw, out=y0)
+        torch.cuda.synchronize()
+        assert torch.equal(y0.view(torch.int16), ref.view(torch.int16)), f"run {r + 1} differs"
+    rows = np.arange(0, 4096, 61)
+    oxq, osx = Q.quantize_mxfp4(xb[rows])
+    owq, osw = Q.quantize_mxfp4(wb)
+    _assert_tol(bf16_to_f64(ref)[rows], G.gemm_mxfp4_ref(oxq, osx, owq, osw), "mxfp4 repeat 4096^2 x 1024")
+
+
 def test_mxfp4_full_size_sampled():
     need_gpu()
     xb, wb = synthetic.mxfp4()
