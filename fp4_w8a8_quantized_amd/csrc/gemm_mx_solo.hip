@@ -10,21 +10,28 @@
 // MFMA that is half the LDS bytes and half the L2 bytes of the two-waves-per-SIMD kernel's
 // 256 x 128 tiles with 64 x 64 wave tiles.
 //
-// LDS: two stages of [X codes 256 x 128 B | W codes 256 x 128 B | X scales 256 x 8 B |
-// W scales 256 x 8 B], 68 KB each, filled by direct-to-LDS loads (16-byte loads for the
-// codes, 4-byte loads for the scales).
+// LDS: two code stages of [X codes 256 x 128 B | W codes 256 x 128 B] (64 KB each), filled
+// by 16-byte direct-to-LDS loads, and the E8M0 scales. With one wave per SIMD a wave whose
+// load cannot issue cannot issue its MFMAs either, and the cost of a load grows with the
+// cache lines it touches: a 4-byte-per-lane scale load touches 32 rows' lines for 256 bytes,
+// as many lines as four code loads. So when K is a multiple of 512 (SC2) the scales of two
+// steps are fetched at once, 16 bytes per row and lane, into two scale stages of
+// [X 256 x 16 B | W 256 x 16 B]: four times fewer scale loads (measured: 4300 -> 3000 cycles
+// per K step at 8192^3 together with the spread code loads below). Otherwise the step's 8
+// scale bytes per row ride in the code stage, two lanes per row.
 //
 // The fragments are not double-buffered (the accumulators take all 256 AGPRs): the MFMAs
 // of a step run in four quarters q = 0..3 (the 64-element slice q of every subtile), and
 // the registers of quarter q are refilled with the next step's quarter q as soon as they
-// are free. Per K step s (stage s % 2 holds step s):
+// are free. Per K step s (code stage s % 2 holds step s):
 //   quarter 0: MFMAs of q = 0; read step s's quarter 3 (its registers were freed by the
 //     previous step's quarter 3); then wait for every outstanding load and fragment read
-//     and one barrier: every wave is done with stage s % 2 and step s + 1 is complete in
-//     stage (s + 1) % 2;
-//   quarter 1: MFMAs of q = 1; read step s + 1's quarter 0 and scale words; issue the loads
-//     of step s + 2 into stage s % 2;
-//   quarters 2, 3: MFMAs; read step s + 1's quarters 1, 2.
+//     and one barrier: every wave is done with code stage s % 2 and step s + 1 is complete;
+//   quarter 1: MFMAs of q = 1; read step s + 1's quarter 0 and scale words; the scale
+//     loads (SC2: of steps s + 2 and s + 3, in even steps);
+//   quarters 1 and 2: the 16 code loads of step s + 2 into code stage s % 2, one after
+//     every other MFMA;
+//   quarters 2, 3: read step s + 1's quarters 1, 2.
 // Every step loads (past the last step, re-fetches of the last step into a stage nobody
 // reads again), so the MFMA sequence has no branches.
 //
@@ -67,6 +74,7 @@ __device__ __forceinline__ void ms_barrier() { asm volatile("s_barrier" ::: "mem
 
 typedef int ms_i32x8 __attribute__((ext_vector_type(8)));
 
+template <bool SC2>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ sx,
                     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ sw, int M, int N,
@@ -74,11 +82,15 @@ gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
   constexpr int BM = kMsBM, BN = kMsBN;
   constexpr int WR = 128, WC = 128;                 // wave tile (2 x 2 waves)
   constexpr int SM = WR / 32, SN = WC / 32;         // 4 x 4 subtiles of 32 x 32
-  constexpr int XT = BM * 128, WT = BN * 128, SXT = BM * 8, SWT = BN * 8;
+  constexpr int XT = BM * 128, WT = BN * 128;
+  // Per-step scales in the code stage (8 bytes per row), or SC2 scale stages of two steps.
+  constexpr int SXT = SC2 ? 0 : BM * 8, SWT = SC2 ? 0 : BN * 8;
   constexpr int STAGE = XT + WT + SXT + SWT;
+  constexpr int SC_BASE = 2 * STAGE, SC_STAGE = (BM + BN) * 16;
   constexpr int NC = (BM + BN) / 32;                // 16-byte-per-lane code loads per wave per step
-  constexpr int NS = (BM + BN) / 128;               // 4-byte-per-lane scale loads per wave per step
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * STAGE];
+  constexpr int NS = SC2 ? 2 : (BM + BN) / 128;     // scale loads per wave per (even, SC2) step
+  static_assert(NC == 16 && NS <= 4, "loads per step assume 256 x 256 tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SC2 ? SC_BASE + 2 * SC_STAGE : 2 * STAGE];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -100,7 +112,8 @@ gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
 
   // Code load c (< NC): X rows 8 (wave + 4 c) .. +7 for c < NC / 2, else W rows
   // 8 (wave + 4 (c - NC / 2)); lane l fetches chunk (l & 7) ^ swizzle of row 8 d + (l >> 3).
-  // Scale load e (< NS): X scale rows 32 (wave + 4 e) .. +31 for e < NS / 2, else W; lane l
+  // Scale load e (< NS), SC2: e = 0 X, 1 W rows 64 wave + l, 16 bytes (steps 2j and 2j + 1)
+  // per lane; otherwise: X scale rows 32 (wave + 4 e) .. +31 for e < NS / 2, else W; lane l
   // fetches bytes 4 (l & 1) .. +3 of the step's 8 scale bytes of row 32 d + (l >> 1).
   uint32_t cvo[NC], svo[NS];
 #pragma unroll
@@ -113,26 +126,34 @@ gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
   }
 #pragma unroll
   for (int e = 0; e < NS; ++e) {
-    const bool isx = e < NS / 2;
-    const int d = wave + 4 * (isx ? e : e - NS / 2);
-    const int r = 32 * d + (lane >> 1);
-    const int row = isx ? min(m0 + r, M - 1) : min(n0 + r, N - 1);
-    svo[e] = (uint32_t)row * (uint32_t)S + 4 * (lane & 1);
+    if constexpr (SC2) {
+      const int r = 64 * wave + lane;
+      const int row = e == 0 ? min(m0 + r, M - 1) : min(n0 + r, N - 1);
+      svo[e] = (uint32_t)row * (uint32_t)S;
+    } else {
+      const bool isx = e < NS / 2;
+      const int d = wave + 4 * (isx ? e : e - NS / 2);
+      const int r = 32 * d + (lane >> 1);
+      const int row = isx ? min(m0 + r, M - 1) : min(n0 + r, N - 1);
+      svo[e] = (uint32_t)row * (uint32_t)S + 4 * (lane & 1);
+    }
   }
   auto dma_code = [&](int ks, int stage, int c) {
     const bool isx = c < NC / 2;
     const int d = wave + 4 * (isx ? c : c - NC / 2);
     ms_dma16(lds0 + stage * STAGE + (isx ? 0 : XT) + d * 1024, cvo[c], (isx ? xq : wq) + (size_t)ks * 128);
   };
+  // Scale load e of step ks into code stage `stage`; SC2: of steps ks and ks + 1 (ks even)
+  // into scale stage `stage`.
   auto dma_scale = [&](int ks, int stage, int e) {
-    const bool isx = e < NS / 2;
-    const int d = wave + 4 * (isx ? e : e - NS / 2);
-    ms_dma4(lds0 + stage * STAGE + XT + WT + (isx ? 0 : SXT) + d * 256, svo[e], (isx ? sx : sw) + (size_t)ks * 8);
-  };
-  constexpr int NL = NC + NS;                        // loads per wave per step
-  auto dma_one = [&](int ks, int stage, int u) {
-    if (u < NC) dma_code(ks, stage, u);
-    else dma_scale(ks, stage, u - NC);
+    if constexpr (SC2) {
+      ms_dma16(lds0 + SC_BASE + stage * SC_STAGE + e * (BM * 16) + wave * 1024, svo[e],
+               (e == 0 ? sx : sw) + (size_t)ks * 8);
+    } else {
+      const bool isx = e < NS / 2;
+      const int d = wave + 4 * (isx ? e : e - NS / 2);
+      ms_dma4(lds0 + stage * STAGE + XT + WT + (isx ? 0 : SXT) + d * 256, svo[e], (isx ? sx : sw) + (size_t)ks * 8);
+    }
   };
 
   const int fr = lane & 31, h = lane >> 5;
@@ -150,13 +171,22 @@ gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
       for (int j = 0; j < SN; ++j) wf[j][q] = *reinterpret_cast<const i32x4*>(base + XT + (wn * WC + 32 * j) * 128 + fo[q]);
     }
   };
-  // The step's 8 scale bytes of the lane's row in each subtile row (X) and column (W).
-  auto read_scales = [&](int stage, u32x2 (&scx)[SM], u32x2 (&scw)[SN]) {
-    const uint8_t* base = lds + stage * STAGE + XT + WT;
+  // The 8 scale bytes of step ks for the lane's row in each subtile row (X) and column (W).
+  auto read_scales = [&](int ks, int stage, u32x2 (&scx)[SM], u32x2 (&scw)[SN]) {
+    const uint8_t* bx;
+    int rs;
+    if constexpr (SC2) {
+      bx = lds + SC_BASE + ((ks >> 1) & 1) * SC_STAGE + (ks & 1) * 8;
+      rs = 16;
+    } else {
+      bx = lds + stage * STAGE + XT + WT;
+      rs = 8;
+    }
+    const uint8_t* bw = bx + (SC2 ? BM * 16 : SXT);
 #pragma unroll
-    for (int i = 0; i < SM; ++i) scx[i] = *reinterpret_cast<const u32x2*>(base + (wm * WR + 32 * i + fr) * 8);
+    for (int i = 0; i < SM; ++i) scx[i] = *reinterpret_cast<const u32x2*>(bx + (wm * WR + 32 * i + fr) * rs);
 #pragma unroll
-    for (int j = 0; j < SN; ++j) scw[j] = *reinterpret_cast<const u32x2*>(base + SXT + (wn * WC + 32 * j + fr) * 8);
+    for (int j = 0; j < SN; ++j) scw[j] = *reinterpret_cast<const u32x2*>(bw + (wn * WC + 32 * j + fr) * rs);
   };
 
   f32x16 acc[SN][SM];
@@ -197,38 +227,48 @@ gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
     quarter(1, cx, cw, [&](int u) {                  // next step's quarter 0, scales, loads
       if (u == 0) read_quarter(Q, 0, 0);
       if (u == 2) read_quarter(Q, 0, 1);
-      if (u == 4) read_scales(Q, nx, nw);
-      if (u < 16) {                                  // NL = 20 loads over the 16 MFMAs
-        dma_one(kl, P, u);
-        if (u < NL - 16) dma_one(kl, P, 16 + u);
+      if (u == 4) read_scales(s + 1, Q, nx, nw);
+      if (!(u & 1)) dma_code(kl, P, u >> 1);
+      if constexpr (SC2) {                           // even steps: steps s + 2, s + 3 (clamped)
+        if (P == 0 && (u & 1) && (u >> 1) < NS) dma_scale(min(s + 2, ksteps - 2), ((s + 2) >> 1) & 1, u >> 1);
+      } else {
+        if ((u & 1) && (u >> 1) < NS) dma_scale(kl, P, u >> 1);
       }
     });
     quarter(2, cx, cw, [&](int u) {
       if (u == 0) read_quarter(Q, 1, 0);
       if (u == 4) read_quarter(Q, 1, 1);
+      if (!(u & 1)) dma_code(kl, P, 8 + (u >> 1));
     });
     quarter(3, cx, cw, [&](int u) {
       if (u == 0) read_quarter(Q, 2, 0);
       if (u == 4) read_quarter(Q, 2, 1);
     });
   };
-  static_assert(NL >= 16 && NL <= 32, "loads are spread over the 16 MFMAs of quarter 1");
 
-  // Prologue: steps 0 and 1 into stages 0 and 1; once step 0 has landed everywhere, its
-  // quarters 0-2 and scale words.
+  // Prologue: steps 0 and 1 into stages 0 and 1 (and the scales of step 0, SC2: of steps
+  // 0 and 1); once step 0 has landed everywhere, its quarters 0-2 and scale words.
   u32x2 scx0[SM], scw0[SN], scx1[SM], scw1[SN];
 #pragma unroll
-  for (int u = 0; u < NL; ++u) dma_one(0, 0, u);
+  for (int c = 0; c < NC; ++c) dma_code(0, 0, c);
 #pragma unroll
-  for (int u = 0; u < NL; ++u) dma_one(min(1, ksteps - 1), 1, u);
-  __builtin_amdgcn_s_waitcnt(ms_wait(NL, 15));
+  for (int e = 0; e < NS; ++e) dma_scale(0, 0, e);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) dma_code(min(1, ksteps - 1), 1, c);
+  if constexpr (!SC2) {
+#pragma unroll
+    for (int e = 0; e < NS; ++e) dma_scale(min(1, ksteps - 1), 1, e);
+    __builtin_amdgcn_s_waitcnt(ms_wait(NC + NS, 15));
+  } else {
+    __builtin_amdgcn_s_waitcnt(ms_wait(NC, 15));
+  }
   ms_barrier();
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
     read_quarter(0, q, 0);
     read_quarter(0, q, 1);
   }
-  read_scales(0, scx0, scw0);
+  read_scales(0, 0, scx0, scw0);
 
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
@@ -243,7 +283,7 @@ gemm_mx_solo_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ 
 
   // ---- epilogue: bf16 tile staged through the freed LDS, whole 16-byte row chunks out.
   constexpr int RS = BN * 2 + 16;                      // padded rows
-  static_assert(BM * RS <= 2 * STAGE, "output tile must fit in the pipeline LDS");
+  static_assert(BM * RS <= (int)sizeof(lds), "output tile must fit in the pipeline LDS");
   // In the 32x32 result (A = W fragment, B = X fragment), lane l holds output row
   // m = 32 i + (l & 31) and the columns 32 j + 8 q + 4 (l >> 5) + r, q, r in 0..3.
 #pragma unroll
@@ -300,7 +340,9 @@ hipError_t launch_gemm_mx_solo(const void* xq, const uint8_t* sx, const void* wq
                                int64_t M, int64_t N, int64_t K, void* y, hipStream_t st) {
   const int tiles_m = (int)((M + kMsBM - 1) / kMsBM);
   const int tiles_n = (int)((N + kMsBN - 1) / kMsBN);
-  hipLaunchKernelGGL(gemm_mx_solo_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMsThreads), 0, st,
+  // Paired scale loads need 16-byte aligned rows of scales: K / 32 a multiple of 16.
+  auto kern = (K % 512 == 0) ? gemm_mx_solo_kernel<true> : gemm_mx_solo_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMsThreads), 0, st,
                      (const uint8_t*)xq, sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)(K / 2),
                      (int)(K / 256), (uint16_t*)y, tiles_m, (int)((N % 8) == 0));
   return hipGetLastError();
