@@ -76,6 +76,7 @@ hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, 
 // W4A16 above 32 tokens (16 above 8192 outputs) with K a multiple of 1024: 32-128 token rows
 // and 16-64 weight rows per workgroup, both staged in LDS one group per K step.
 bool use_w4a16_mid(int64_t M, int64_t N, int64_t K);
+bool use_w4a16_gemv(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w4a16_mid(const void* x, const void* wq, const uint16_t* sc, int64_t M,
                                  int64_t N, int64_t K, void* y, hipStream_t st);
 // INT8 form of the MXFP4 two-waves-per-SIMD kernel (256 x 128 tiles, 32x32x32 MFMAs).

@@ -16,6 +16,15 @@
 // group's sum: the group's fp32 partial is multiplied by S[n, group] and accumulated, which
 // keeps every product exact (S q would need up to 14 significant bits). The waves' sums
 // meet in LDS. M above 128 is processed in slices of 128 rows (each re-reads W).
+//
+// GEMV (one token, K a multiple of 2048 up to 16384): the weight stream in whole rows. A
+// 16-byte-per-lane load of the tile kernel above covers 16 rows x 64 bytes, half a cache line
+// per row. Here each wave reads whole weight rows, a kilobyte of one row per load (8 full
+// lines); each lane keeps its K / 64 elements of X in registers for the whole kernel,
+// dequantizes its 32 codes per load with the biased conversion below and takes the products
+// with v_dot2 (two bf16 products accumulated in fp32 per instruction); the row's sum is reduced
+// across the wave with DPP moves. From two tokens on, the MFMA kernel above is faster (the
+// dot products grow with the tokens while the MFMA's are free up to 16).
 #include "common.h"
 #include "internal.h"
 
@@ -203,6 +212,121 @@ hipError_t launch_w4a16_slice(const void* x, const void* wq, const uint16_t* sc,
   return launch_w4a16_cfg<8, 4, 1>(x, wq, sc, M, N, K, y, st);
 }
 
+
+// Eight 4-bit two's-complement codes n (one word, element 2i in the low nibble of byte i) as
+// four bf16 pairs of 136 + n, exactly: n + 8 = n ^ 8 is the unsigned nibble u, and the bf16
+// pattern 0x4300 | u is 128 + u (one unit in the last place at 128). That is 1.5 integer
+// instructions per element (xor, two masks, a byte permute and an or per pair); the bias 136
+// comes off each row's sum as 136 sum_k x_k. Every product x (136 + n) is exact in fp32.
+__device__ __forceinline__ void int4x8_to_bf16_biased(uint32_t w, uint32_t (&p)[4]) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;   // u0 u2 u4 u6 | u1 u3 u5 u7
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    p[i] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + i) << 16) | (uint32_t)i) | 0x43004300u;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// v + DPP-moved v: a lane of a row that the row mask leaves out adds 0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float gv_dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+// Sum of v over the 64 lanes of the wave, in lane 63: pairs and quads (quad_perm), the 16 lanes
+// of a row (row_ror 4, 8), then rows 0 + 1 and 2 + 3 (row_bcast15 into rows 1 and 3) and all
+// four (row_bcast31 into rows 2 and 3).
+__device__ __forceinline__ float gv_wave_sum(float v) {
+  v = gv_dpp_add<0xB1, 0xF>(v);     // quad_perm [1, 0, 3, 2]
+  v = gv_dpp_add<0x4E, 0xF>(v);     // quad_perm [2, 3, 0, 1]
+  v = gv_dpp_add<0x124, 0xF>(v);    // row_ror 4
+  v = gv_dpp_add<0x128, 0xF>(v);    // row_ror 8
+  v = gv_dpp_add<0x142, 0xA>(v);    // row_bcast15
+  v = gv_dpp_add<0x143, 0xC>(v);    // row_bcast31
+  return v;
+}
+
+constexpr int kGvChunk = 2048;          // K elements per load of a whole wave (one kilobyte of codes)
+
+// Wave w of the grid takes weight rows w, w + W, ... (W waves in all), one row in flight: L
+// loads of 16 bytes per lane (chunk 64 t + l of the row, K offsets 32 (64 t + l) .. +31).
+template <int L>
+__global__ void __launch_bounds__(256)
+gemm_w4a16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
+                       const uint16_t* __restrict__ sc, int N, int K, int groups,
+                       uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), GW = gridDim.x * 4;
+  const int cnt = gw < N ? (N - 1 - gw) / GW + 1 : 0;
+  const int64_t kb = K / 2;
+  u32x4 wb[L];
+  uint16_t sb[L];
+  auto load = [&](int i) {
+    const int n = gw + GW * i;
+    const u32x4* wr = reinterpret_cast<const u32x4*>(wq + (int64_t)n * kb);
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+      wb[t] = __builtin_nontemporal_load(wr + 64 * t + lane);
+      sb[t] = sc[(int64_t)n * groups + ((64 * t + lane) >> 2)];
+    }
+  };
+  if (cnt > 0) load(0);
+  // X once per workgroup into LDS (its four waves need the same values), then each lane's
+  // chunks and 136 times their sums (the conversion's bias).
+  __shared__ u32x4 xl[256 * L];
+#pragma unroll
+  for (int t = 0; t < L; ++t) xl[256 * t + threadIdx.x] = reinterpret_cast<const u32x4*>(x)[256 * t + threadIdx.x];
+  __syncthreads();
+  uint32_t xw[L][16];
+  float xb[L];
+#pragma unroll
+  for (int t = 0; t < L; ++t) {
+    const u32x4* xp = xl + 4 * (64 * t + lane);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = xp[q];
+      xw[t][4 * q] = v.x; xw[t][4 * q + 1] = v.y; xw[t][4 * q + 2] = v.z; xw[t][4 * q + 3] = v.w;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum += __uint_as_float(xw[t][e] << 16) + __uint_as_float(xw[t][e] & 0xFFFF0000u);
+    xb[t] = 136.0f * sum;
+  }
+  for (int i = 0; i < cnt; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < L; ++t) {
+      const uint32_t w4[4] = {wb[t].x, wb[t].y, wb[t].z, wb[t].w};
+      float d = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t p[4];
+        int4x8_to_bf16_biased(w4[j], p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[e]),
+                                              __builtin_bit_cast(bf16x2, xw[t][4 * j + e]), d, false);
+      }
+      acc = __builtin_fmaf(d - xb[t], (float)__builtin_bit_cast(_Float16, sb[t]), acc);
+    }
+    if (i + 1 < cnt) load(i + 1);
+    acc = gv_wave_sum(acc);
+    if (lane == 63) y[gw + GW * i] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
+  }
+}
+
+template <int L>
+hipError_t launch_w4a16_gemv(const void* x, const void* wq, const uint16_t* sc, int64_t N, int64_t K,
+                             void* y, hipStream_t st) {
+  // About two rows per wave, at most 1024 workgroups (measured at 4096 and 14336 rows).
+  const int64_t want = (N + 7) / 8;
+  const int blocks = (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
+  hipLaunchKernelGGL((gemm_w4a16_gemv_kernel<L>), dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const uint16_t*)x, (const uint8_t*)wq, sc, (int)N, (int)K, (int)(K / kG),
+                     (uint16_t*)y);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, uint16_t* sc,
@@ -213,8 +337,24 @@ hipError_t launch_quantize_int4(const void* w, int64_t N, int64_t K, void* q, ui
   return hipGetLastError();
 }
 
+bool use_w4a16_gemv(int64_t M, int64_t N, int64_t K) {
+  return M == 1 && K % kGvChunk == 0 && K / kGvChunk <= 8 && N >= 1 && N <= INT32_MAX;
+}
+
 hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
                              int64_t K, void* y, hipStream_t st) {
+  if (use_w4a16_gemv(M, N, K)) {
+    switch (K / kGvChunk) {
+      case 1: return launch_w4a16_gemv<1>(x, wq, sc, N, K, y, st);
+      case 2: return launch_w4a16_gemv<2>(x, wq, sc, N, K, y, st);
+      case 3: return launch_w4a16_gemv<3>(x, wq, sc, N, K, y, st);
+      case 4: return launch_w4a16_gemv<4>(x, wq, sc, N, K, y, st);
+      case 5: return launch_w4a16_gemv<5>(x, wq, sc, N, K, y, st);
+      case 6: return launch_w4a16_gemv<6>(x, wq, sc, N, K, y, st);
+      case 7: return launch_w4a16_gemv<7>(x, wq, sc, N, K, y, st);
+      default: return launch_w4a16_gemv<8>(x, wq, sc, N, K, y, st);
+    }
+  }
   if (use_w4a16_mid(M, N, K)) return launch_gemm_w4a16_mid(x, wq, sc, M, N, K, y, st);
   for (int64_t m0 = 0; m0 < M; m0 += 128) {
     const int64_t mr = M - m0 < 128 ? M - m0 : 128;

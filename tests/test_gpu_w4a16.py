@@ -85,6 +85,20 @@ def test_gemm_w4a16_ragged(M, N, K):
     _gemm_compare(xb, wb, f"{M}x{N}x{K}")
 
 
+# one token with K a multiple of 2048 up to 16384 takes the whole-row GEMV: one to eight
+# kilobyte loads per row, N below, at and above one row per wave of the grid (1024
+# workgroups of 4 waves), N = 1; two tokens and K = 18432 take the tile kernel beside it
+@pytest.mark.parametrize("M,N,K", [(1, 1, 2048), (1, 4099, 4096), (1, 5, 6144), (1, 1001, 10240),
+                                   (1, 257, 16384), (1, 9000, 8192), (1, 4096, 14336), (2, 300, 4096),
+                                   (1, 130, 18432), (1, 12000, 2048)])
+def test_gemm_w4a16_gemv(M, N, K):
+    need_gpu()
+    rng = np.random.default_rng(M * 7 + N * 5 + K)
+    xb = _bf16(rng.standard_normal((M, K)))
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02)
+    _gemm_compare(xb, wb, f"gemv {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("N", synthetic.DECODE_NS)
 def test_gemm_w4a16_decode_sweep(N):
     """The decode sweep's shapes (M in 1, 8, 32, 128; K = 4096) on its activations."""
