@@ -357,6 +357,31 @@ def _launch_mean_s(c: Ctx, fn, reps: int) -> float:
     return e0.elapsed_time(e1) * 1e-3 / reps
 
 
+def _graph_mean_s(c: Ctx, fn, reps: int) -> float:
+    """Mean duration in seconds of fn(0, s) .. fn(reps - 1, s) captured into one HIP graph on a
+    side stream s and replayed once between two HIP events: the kernels back to back with no
+    host launch cost between them (a kernel of a few microseconds launched from Python through
+    the C ABI is otherwise bounded by the host's launch rate). The library records no memset
+    or allocation, so its launches capture as they are."""
+    torch = c.torch
+    side = torch.cuda.Stream(device=c.dev)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(reps):
+                fn(i, side.cuda_stream)
+    torch.cuda.synchronize()
+    g.replay()                                          # warm: the graph's first launch
+    torch.cuda.synchronize()
+    e0, e1 = c.event(), c.event()
+    e0.record(c.stream)
+    g.replay()
+    e1.record(c.stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / reps
+
+
 # ----------------------------------------------------------------------------- prefill
 def prefill_cpu_baseline(layers, rows: int):
     """The oracle as it stands on a sample of the same step: `rows` tokens of each linear
@@ -819,24 +844,26 @@ def run_decode(args, c: Ctx):
                 sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
 
-                def quant(i):
-                    c.check(L.w8a8_quantize_per_token(x.data_ptr(), M, K, fmt, xq.data_ptr(), sx.data_ptr(), sh))
+                def quant(i, s=sh):
+                    c.check(L.w8a8_quantize_per_token(x.data_ptr(), M, K, fmt, xq.data_ptr(), sx.data_ptr(), s))
 
-                def gemm(i):
+                def gemm(i, s=sh):
                     c.check(L.w8a8_gemm(xq.data_ptr(), sx.data_ptr(), ws[i % copies].data_ptr(),
-                                        sw.data_ptr(), M, N, K, fmt, y.data_ptr(), sh))
+                                        sw.data_ptr(), M, N, K, fmt, y.data_ptr(), s))
 
                 for i in range(max(args.warmup, 3)):
                     quant(i)
                     gemm(i)
                 R = 3 * copies
-                q_us = _launch_mean_s(c, quant, R) * 1e6
-                g_us = _launch_mean_s(c, gemm, R) * 1e6
+                q_us = _graph_mean_s(c, quant, R) * 1e6
+                g_us = _graph_mean_s(c, gemm, R) * 1e6
+                ge_us = _launch_mean_s(c, gemm, R) * 1e6
                 byt = N * K + M * K + 2 * M * N + 4 * (M + N)
                 flops = 2.0 * M * N * K
                 attain = min(FP8_PEAK_TFLOPS, flops / byt * HBM_PEAK_GBPS / 1e3)   # TFLOP/s
                 cases.append({"M": M, "N": N, "fmt": "fp8" if fmt == 0 else "int8",
-                              "gemm_us": round(g_us, 2), "quant_us": round(q_us, 2),
+                              "gemm_us": round(g_us, 2), "gemm_eager_us": round(ge_us, 2),
+                              "quant_us": round(q_us, 2),
                               "gemm_GBps": round(byt / g_us / 1e3, 1),
                               "gemm_tflops": round(flops / g_us / 1e6, 2),
                               "roofline_frac": round(flops / g_us / 1e6 / attain, 4)})
@@ -856,6 +883,9 @@ def run_decode(args, c: Ctx):
     rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
     rec["cases"] = cases
+    rec["timing"] = ("per case: 3 x (weight copies) launches over rotating weights captured in one HIP graph "
+                     "and replayed (gemm_us, quant_us); gemm_eager_us: the same launches issued from the "
+                     "host back to back")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = decode_cpu_baseline()
     return rec
@@ -882,16 +912,18 @@ def run_w4a16(args, c: Ctx):
             x = xall[:M]
             y = torch.empty((M, N), dtype=torch.bfloat16, device=c.dev)
 
-            def launch(i):
+            def launch(i, s=sh):
                 c.check(L.w8a8_gemm_w4a16(x.data_ptr(), qs[i % copies].data_ptr(), ss[i % copies].data_ptr(),
-                                          M, N, K, y.data_ptr(), sh))
+                                          M, N, K, y.data_ptr(), s))
 
             for i in range(max(args.warmup, 3)):
                 launch(i)
-            g_us = _launch_mean_s(c, launch, 3 * copies) * 1e6
+            g_us = _graph_mean_s(c, launch, 3 * copies) * 1e6
+            ge_us = _launch_mean_s(c, launch, 3 * copies) * 1e6
             byt = wbytes + 2 * M * K + 2 * M * N
             flops = 2.0 * M * N * K
-            cases.append({"M": M, "N": N, "gemm_us": round(g_us, 2), "gemm_GBps": round(byt / g_us / 1e3, 1),
+            cases.append({"M": M, "N": N, "gemm_us": round(g_us, 2), "gemm_eager_us": round(ge_us, 2),
+                          "gemm_GBps": round(byt / g_us / 1e3, 1),
                           "gemm_tflops": round(flops / g_us / 1e6, 3),
                           "hbm_frac": round(byt / g_us / 1e3 / HBM_PEAK_GBPS, 4)})
         del qs, ss
@@ -907,6 +939,8 @@ def run_w4a16(args, c: Ctx):
     rec["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
     rec["cases"] = cases
+    rec["timing"] = ("per case: 3 x (weight copies) launches over rotating weights captured in one HIP graph "
+                     "and replayed (gemm_us); gemm_eager_us: the same launches issued from the host back to back")
     if not args.no_cpu_baseline:
         from oracle import w4a16 as W4
         wb = synthetic.decode_w(4096)

@@ -126,6 +126,33 @@ __device__ __forceinline__ void epi_dispatch(int act, bool bias, F&& f) {
   }
 }
 
+// Sum of v over the 64 lanes of the wave, in lane 63, by DPP moves: pairs and quads
+// (quad_perm), the 16 lanes of a row (row_ror 4, 8), then rows 0 + 1 and 2 + 3 (row_bcast15
+// into rows 1 and 3) and all four (row_bcast31 into rows 2 and 3). A lane of a row that the
+// row mask leaves out adds 0. Integer sums are exact.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_moved(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+template <class T>
+__device__ __forceinline__ T wave_sum_dpp(T v) {
+  auto step = [](T a, int moved) {
+    if constexpr (std::is_same<T, float>::value) return a + __int_as_float(moved);
+    else return a + moved;
+  };
+  auto bits = [](T a) {
+    if constexpr (std::is_same<T, float>::value) return __float_as_int(a);
+    else return a;
+  };
+  v = step(v, dpp_moved<0xB1, 0xF>(bits(v)));     // quad_perm [1, 0, 3, 2]
+  v = step(v, dpp_moved<0x4E, 0xF>(bits(v)));     // quad_perm [2, 3, 0, 1]
+  v = step(v, dpp_moved<0x124, 0xF>(bits(v)));    // row_ror 4
+  v = step(v, dpp_moved<0x128, 0xF>(bits(v)));    // row_ror 8
+  v = step(v, dpp_moved<0x142, 0xA>(bits(v)));    // row_bcast15
+  v = step(v, dpp_moved<0x143, 0xC>(bits(v)));    // row_bcast31
+  return v;
+}
+
 // clamp(q, +-448); a NaN stays NaN (both comparisons are false).
 __device__ __forceinline__ float clamp448(float q) {
   return q > 448.f ? 448.f : (q < -448.f ? -448.f : q);

@@ -7,6 +7,8 @@
 // epilogue; "Low-bit LLM Weights and Activations" §3.4).
 //
 // Dispatch by shape:
+//  - one token (K a multiple of 1024 up to 16384): whole weight rows per wave on the vector
+//    unit (gemm_gemv.hip);
 //  - narrow tiles sized to the token count (gemm_narrow.hip) where they measured faster: up
 //    to 64 tokens on layers wider than 4096 outputs, 65-128 tokens above 8192 outputs, and
 //    256-512 tokens where one round of 128 x 64 tiles covers the output;
@@ -25,6 +27,7 @@ namespace w8a8 {
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                        const Epilogue& ep) {
+  if (use_gemm_gemv(M, N, K)) return launch_gemm_gemv(xq, sx, wq, sw, N, K, fmt, y, st, ep);
   if (use_gemm_narrow(M, N, K)) return launch_gemm_narrow(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (M <= 32) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (M <= 512 && mid_weight_rows(M, N) != 0)

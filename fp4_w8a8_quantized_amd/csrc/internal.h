@@ -101,6 +101,11 @@ hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float*
 // 4 waves, K steps through an LDS ring): where it measured faster than the other few-token
 // and mid-size kernels (use_gemm_narrow).
 bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
+// One token, K a multiple of 1024 up to 16384: whole weight rows per wave on the vector unit
+// (gemm_gemv.hip).
+bool use_gemm_gemv(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_gemv(const void* xq, const float* sx, const void* wq, const float* sw, int64_t N,
+                            int64_t K, int fmt, void* y, hipStream_t st, const Epilogue& ep);
 hipError_t launch_gemm_narrow(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                               const Epilogue& ep);

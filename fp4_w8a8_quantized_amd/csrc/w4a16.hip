@@ -228,24 +228,6 @@ __device__ __forceinline__ void int4x8_to_bf16_biased(uint32_t w, uint32_t (&p)[
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// v + DPP-moved v: a lane of a row that the row mask leaves out adds 0.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float gv_dpp_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
-}
-// Sum of v over the 64 lanes of the wave, in lane 63: pairs and quads (quad_perm), the 16 lanes
-// of a row (row_ror 4, 8), then rows 0 + 1 and 2 + 3 (row_bcast15 into rows 1 and 3) and all
-// four (row_bcast31 into rows 2 and 3).
-__device__ __forceinline__ float gv_wave_sum(float v) {
-  v = gv_dpp_add<0xB1, 0xF>(v);     // quad_perm [1, 0, 3, 2]
-  v = gv_dpp_add<0x4E, 0xF>(v);     // quad_perm [2, 3, 0, 1]
-  v = gv_dpp_add<0x124, 0xF>(v);    // row_ror 4
-  v = gv_dpp_add<0x128, 0xF>(v);    // row_ror 8
-  v = gv_dpp_add<0x142, 0xA>(v);    // row_bcast15
-  v = gv_dpp_add<0x143, 0xC>(v);    // row_bcast31
-  return v;
-}
-
 constexpr int kGvChunk = 2048;          // K elements per load of a whole wave (one kilobyte of codes)
 
 // Wave w of the grid takes weight rows w, w + W, ... (W waves in all), one row in flight: L
@@ -310,7 +292,7 @@ gemm_w4a16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
       acc = __builtin_fmaf(d - xb[t], (float)__builtin_bit_cast(_Float16, sb[t]), acc);
     }
     if (i + 1 < cnt) load(i + 1);
-    acc = gv_wave_sum(acc);
+    acc = wave_sum_dpp(acc);
     if (lane == 63) y[gw + GW * i] = (uint16_t)(pack_bf16x2(acc, 0.f) & 0xFFFFu);
   }
 }

@@ -84,6 +84,29 @@ SKINNY_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (6
                 (513, 1000, 256), (40, 4100, 512), (64, 40000, 256), (48, 33000, 128)]
 
 
+# One token with K a multiple of 1024 up to 16384 takes the whole-row vector kernel: one to
+# sixteen kilobyte loads per row, N below and above the grid's 4096 waves (several rows per
+# wave), and beside it K = 17408 and K = 640 (the tiled kernels).
+GEMV_CASES = [(1, 1, 1024), (1, 7, 3072), (1, 4097, 4096), (1, 14336, 4096), (1, 4096, 14336),
+              (1, 300, 16384), (1, 9001, 2048), (1, 20000, 1024), (1, 130, 17408), (1, 500, 640)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_CASES)
+def test_fp8_one_token(M, N, K):
+    need_gpu()
+    xb, wb = _xw(M, N, K, 17 * N + K)
+    _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", GEMV_CASES)
+def test_int8_one_token(M, N, K):
+    """INT8 sums are exact in any order: bit-exact against the oracle's chain."""
+    need_gpu()
+    xb, wb = _xw(M, N, K, 19 * N + K)
+    xcal, _ = _xw(64, 1, K, K + 3)
+    _int8_chain(xb, xcal, wb, 0.5, f"{M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K", SKINNY_CASES)
 def test_fp8_few_tokens(M, N, K):
     need_gpu()
