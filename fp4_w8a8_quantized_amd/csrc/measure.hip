@@ -38,7 +38,8 @@ hipError_t launch_sclk_probe(uint64_t* out, int blocks, int64_t ticks, hipStream
 // byte per element, as the per-token and static quantizers do. Each element's output byte
 // is the high byte of its bf16 input (no arithmetic to speak of). Thread t of block b
 // handles the 16-byte input chunks b * 1024 + t + 256 i, i < 4, loading all four before
-// storing, so that every thread keeps 64 bytes of loads in flight.
+// storing, so that every thread keeps 64 bytes of loads in flight. Loads and stores use the
+// quantizers' cache policy (non-temporal loads, ordinary stores).
 __global__ void __launch_bounds__(256) stream_probe_kernel(const u32x4* __restrict__ x, int64_t nchunks,
                                                            u32x2* __restrict__ y) {
   const int64_t c0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
@@ -53,7 +54,7 @@ __global__ void __launch_bounds__(256) stream_probe_kernel(const u32x4* __restri
     u32x2 o;
     o.x = ((a.x >> 8) & 0xFFu) | ((a.x >> 16) & 0xFF00u) | (((a.y >> 8) & 0xFFu) << 16) | ((a.y >> 24) << 24);
     o.y = ((a.z >> 8) & 0xFFu) | ((a.z >> 16) & 0xFF00u) | (((a.w >> 8) & 0xFFu) << 16) | ((a.w >> 24) << 24);
-    __builtin_nontemporal_store(o, y + c0 + 256 * i);
+    y[c0 + 256 * i] = o;
   }
 }
 

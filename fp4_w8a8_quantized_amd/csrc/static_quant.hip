@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const u32x4* __restri
         o.x = pack_e4m3x4(f[0], f[1], f[2], f[3]);
         o.y = pack_e4m3x4(f[4], f[5], f[6], f[7]);
       }
-      __builtin_nontemporal_store(o, q + c);
+      __builtin_nontemporal_store(o, q + c);   // measured faster here than an ordinary store
     }
   };
   if (shortcut) run(std::true_type{});
