@@ -230,7 +230,10 @@ hipError_t launch_quantize_block(const void* w, int64_t N, int64_t K, void* q, f
 // MXFP4: one thread per 16-byte chunk (8 elements), four consecutive lanes form a
 // 32-element block. Scale exponent e = floor(log2 amax) - 2 (E2M1's top binade is 2^2),
 // clamped to [-127, 127], 0 for an all-zero block; elements x * 2^-e (exact) are
-// rounded to E2M1 half-to-even and saturated to +-6.
+// rounded to E2M1 half-to-even and saturated to +-6. A block holding an infinity or a NaN
+// gets the E8M0 NaN code 0xFF (the OCP MX format's one special scale value; the pages name
+// the E8M0 scale but not its special value) and element codes 0, so it decodes to NaN: E2M1
+// itself has no non-finite values.
 __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __restrict__ x,
                                                           int64_t nchunk, uint8_t* __restrict__ q,
                                                           uint8_t* __restrict__ sc) {
@@ -241,13 +244,19 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   float amax = chunk_absmax(v);
   amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
   amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
+  // non-finite bf16: all exponent bits set
+  int bad = 0;
+  for (const uint32_t h : {v.x, v.y, v.z, v.w})
+    bad |= (h & 0x7F80u) == 0x7F80u || (h & 0x7F800000u) == 0x7F800000u;
+  bad |= __shfl_xor(bad, 1, kWave);
+  bad |= __shfl_xor(bad, 2, kWave);
   if (!live) return;
   int e = 0;
-  if (amax > 0.0f) {
+  if (amax > 0.0f && !bad) {
     e = __builtin_amdgcn_frexp_expf(amax) - 1 - 2;   // floor(log2 amax) - 2
     e = max(-127, min(127, e));
   }
-  if ((threadIdx.x & 3) == 0) sc[c >> 2] = (uint8_t)(e + 127);
+  if ((threadIdx.x & 3) == 0) sc[c >> 2] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
   // gfx950's converter divides each bf16 of a pair by the scale's power of two (only the
   // scale's exponent field is read: 2^e is passed as the fp32 pattern (e + 127) << 23),
   // rounds half to even onto the E2M1 grid and saturates at 6, element 2i to the low
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(256) void quant_mxfp4_kernel(const uint16_t* __rest
   out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2, w[3]), scl, 3);
 #pragma unroll
   for (int i = 0; i < 4; ++i) sgn |= (((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u)) << (8 * i);
-  reinterpret_cast<uint32_t*>(q)[c] = out | sgn;
+  reinterpret_cast<uint32_t*>(q)[c] = bad ? 0u : out | sgn;
 }
 
 hipError_t launch_quantize_mxfp4(const void* x, int64_t R, int64_t K, void* q, uint8_t* sc,

@@ -28,6 +28,10 @@ Readings where the pages leave a step open:
   [-127, 127]; scale code e + 127; elements x / 2^e are encoded with saturation to +-6.
   A block whose amax is 0 gets code 127 (scale 1), following the emulation's rule that a
   zero scale becomes 1 ([P-FP8FP4] ``nvfp4``).
+* A 32-element MX block that holds an infinity or a NaN (the pages do not say): the
+  E8M0 scale code 255, the format's one special value (NaN), and element codes 0 (E2M1
+  has no special values). Such a block decodes to NaN, so a non-finite input stays
+  non-finite through the GEMM.
 """
 
 from __future__ import annotations
@@ -162,8 +166,11 @@ def quantize_mxfp4(x_bits: np.ndarray):
     if K % 32:
         raise ValueError("K must be a multiple of 32")
     xb = x.reshape(R, K // 32, 32)
+    bad = ~np.all(np.isfinite(xb), axis=-1)        # blocks with an infinity or a NaN
+    xb = np.where(bad[..., None], 0.0, xb)
     amax = np.max(np.abs(xb), axis=-1)
     e = mx_scale_exponent(amax)
     scaled = xb / np.ldexp(1.0, e)[..., None]      # exact: division by a power of two
     codes = e2m1_encode(scaled).reshape(R, K)
-    return pack_e2m1(codes), (e + 127).astype(np.uint8)
+    sc = np.where(bad, 255, e + 127).astype(np.uint8)
+    return pack_e2m1(codes), sc

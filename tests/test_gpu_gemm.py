@@ -393,6 +393,37 @@ def test_mxfp4_scales_span_binades(M, N, K):
     _mx_compare(xb, wb, f"binade-scaled mxfp4 {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K", [(17, 130, 512), (300, 549, 1024), (4096, 4100, 256)])
+def test_mxfp4_non_finite_blocks(M, N, K):
+    """Infinities and NaNs scattered over both operands: their blocks carry the E8M0 NaN
+    code, and the GEMM gives NaN in exactly the rows of X and columns of W that hold one,
+    the oracle's value within the tolerance everywhere else. The last shape runs on the
+    256 x 256 one-wave-per-SIMD kernel, the others on the two-waves-per-SIMD kernel."""
+    need_gpu()
+    rng = np.random.default_rng(M + 3 * N + K)
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((N, K)) * 0.02
+    for a, vals in ((x, (np.inf, -np.inf, np.nan)), (w, (np.nan, np.inf, -np.inf))):
+        idx = rng.choice(a.size, size=max(3, a.shape[0] // 40), replace=False)
+        a.flat[idx] = rng.choice(vals, size=len(idx))
+    xb, wb = _bf16(x), _bf16(w)
+    xq, sx = w8.quantize_mxfp4(to_dev_bf16(xb))
+    wq, sw = w8.quantize_mxfp4(to_dev_bf16(wb))
+    y = w8.gemm_mxfp4(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    oxq, osx = Q.quantize_mxfp4(xb)
+    owq, osw = Q.quantize_mxfp4(wb)
+    assert np.array_equal(bits_u8(sx), osx) and np.array_equal(bits_u8(xq), oxq)
+    assert np.array_equal(bits_u8(sw), osw) and np.array_equal(bits_u8(wq), owq)
+    ref = G.gemm_mxfp4_ref(oxq, osx, owq, osw)
+    nan_ref = np.isnan(ref)
+    assert np.array_equal(nan_ref, np.isnan(x).any(1)[:, None] | np.isinf(x).any(1)[:, None]
+                          | (np.isnan(w).any(1) | np.isinf(w).any(1))[None, :])
+    yg = bf16_to_f64(y)
+    assert np.array_equal(np.isnan(yg), nan_ref), f"{M}x{N}x{K}: NaN pattern differs"
+    _assert_tol(yg[~nan_ref], ref[~nan_ref], f"non-finite mxfp4 {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K,binades", [(4097, 4100, 512, False), (4096, 4352, 768, True),
                                             (4352, 4096, 256, True)])
 def test_mxfp4_wide_tiles(M, N, K, binades):

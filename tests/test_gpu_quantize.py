@@ -162,6 +162,29 @@ def test_mxfp4_quant(R, K):
     assert np.array_equal(bits_u8(q), qo), first_mismatch(bits_u8(q), qo)
 
 
+def test_mxfp4_quant_non_finite_blocks():
+    """Every non-finite bf16 pattern (both infinities, every NaN payload) once in a block of
+    otherwise finite values, and blocks whose only non-finite element sits in each of the
+    four 8-element chunks: the E8M0 NaN code and zero element codes, bit for bit, with the
+    neighbouring blocks untouched."""
+    need_gpu()
+    allv = synthetic.bf16_bits_to_f32(np.arange(65536, dtype=np.uint16)).astype(np.float64)
+    bad = allv[~np.isfinite(allv)]
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((len(bad) // 4 + 4, 4 * 32)) * 3.0
+    for i, b in enumerate(bad):                 # block i % 4 of row i // 4, element (7 i) % 32
+        x[i // 4, 32 * (i % 4) + (7 * i) % 32] = b
+    for c in range(4):                          # last rows: one infinity in chunk c of block c
+        x[-4 + c, 32 * c + 8 * c + 3] = np.inf if c % 2 else -np.inf
+    xb = _bf16(x)
+    q, s = w8.quantize_mxfp4(to_dev_bf16(xb))
+    torch.cuda.synchronize()
+    qo, so = Q.quantize_mxfp4(xb)
+    assert np.count_nonzero(so == 255) == len(bad) + 4
+    assert np.array_equal(bits_u8(s), so), first_mismatch(bits_u8(s), so)
+    assert np.array_equal(bits_u8(q), qo), first_mismatch(bits_u8(q), qo)
+
+
 def test_mxfp4_quant_all_bf16_patterns():
     need_gpu()
     allv = synthetic.bf16_bits_to_f32(np.arange(65536, dtype=np.uint16)).astype(np.float64)

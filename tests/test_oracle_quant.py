@@ -6,6 +6,7 @@ import numpy as np
 
 import synthetic
 from oracle import formats as F
+from oracle import gemm as G
 from oracle import quant as Q
 from tests import golden
 
@@ -219,6 +220,48 @@ def test_mxfp4_bruteforce_and_properties():
             # the largest element lands on 4 or 6 (codes 6, 7), never above 6
             j = int(np.argmax(np.abs(xf[r, b * 32:(b + 1) * 32])))
             assert (c[j] & 7) in (6, 7)
+
+
+def test_mxfp4_non_finite_blocks():
+    """A block with an infinity or a NaN gets the E8M0 NaN code 255 and zero element codes;
+    the other blocks of the row are quantized as if it were not there."""
+    x = np.zeros((3, 96))
+    x[0, 5] = np.inf                            # block 0 of row 0
+    x[0, 40] = 3.0                              # block 1 of row 0: unaffected
+    x[1, 70] = np.nan                           # block 2 of row 1
+    x[1, 71] = 1.0
+    x[2, 10] = -np.inf                          # row 2, block 0
+    x[2, 64:96] = 0.5                           # row 2, block 2: unaffected
+    qp, sc = Q.quantize_mxfp4(_bf16(x))
+    codes = F.unpack_e2m1(qp)
+    assert sc[0].tolist() == [255, 126, 127] and np.all(codes[0, :32] == 0)
+    assert codes[0, 40] == 7                    # 3 / 2^-1 = 6
+    assert sc[1].tolist() == [127, 127, 255] and np.all(codes[1, 64:] == 0)
+    assert sc[2].tolist() == [255, 127, 124]    # 127 + floor(log2 0.5) - 2
+    assert np.all(codes[2, :32] == 0)
+    assert np.all(codes[2, 64:] == 6)           # 0.5 / 2^-3 = 4, grid code 6
+    # decoding: NaN for the marked blocks only
+    dec = F.e2m1_decode(codes) * np.repeat(F.e8m0_decode(sc), 32, axis=1)
+    assert np.all(np.isnan(dec[0, :32])) and np.all(np.isfinite(dec[0, 32:]))
+    assert np.all(np.isnan(dec[1, 64:])) and np.all(np.isfinite(dec[1, :64]))
+
+
+def test_mxfp4_non_finite_block_through_the_gemm():
+    """A NaN-scaled block of X makes its row of the output NaN, one of W its column; every
+    other output equals the reference without the non-finite element's row or column."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 128))
+    w = rng.standard_normal((4, 128)) * 0.05
+    x[2, 33] = np.inf
+    w[1, 100] = np.nan
+    xq, sx = Q.quantize_mxfp4(_bf16(x))
+    wq, sw = Q.quantize_mxfp4(_bf16(w))
+    y = G.gemm_mxfp4_ref(xq, sx, wq, sw)
+    assert np.all(np.isnan(y[2])) and np.all(np.isnan(y[:, 1]))
+    keep_r = [0, 1, 3, 4]
+    keep_c = [0, 2, 3]
+    ref = G.gemm_mxfp4_ref(xq[keep_r], sx[keep_r], wq[keep_c], sw[keep_c])
+    assert np.array_equal(y[np.ix_(keep_r, keep_c)], ref)
 
 
 def test_mxfp4_zero_block():
