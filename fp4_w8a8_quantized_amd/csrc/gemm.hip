@@ -9,14 +9,13 @@
 // Dispatch by shape:
 //  - one token (K a multiple of 1024 up to 16384): whole weight rows per wave on the vector
 //    unit (gemm_gemv.hip);
-//  - narrow tiles sized to the token count (gemm_narrow.hip) where they measured faster: up
-//    to 64 tokens on layers wider than 4096 outputs, 65-128 tokens above 8192 outputs, and
-//    256-512 tokens where one round of 128 x 64 tiles covers the output;
-//  - otherwise up to 32 tokens (the weights dominate the traffic): the weight-streaming
-//    kernel of gemm_skinny.hip;
-//  - 33-512 tokens, where one round of workgroups covers the output: gemm_mid.hip, whose
-//    workgroups hold up to 256 token rows against 16-128 weight rows (a 256-row tile would
-//    leave most CUs idle on 4096-wide layers);
+//  - 2-128 tokens, and 256-512 tokens where one round of 128 x 64 tiles covers the output:
+//    narrow tiles sized to the token count (gemm_narrow.hip), except 65-128 tokens on
+//    4097-8192 outputs;
+//  - one token that the vector kernel does not take: the weight-streaming split-K kernel
+//    (gemm_skinny.hip);
+//  - otherwise up to 512 tokens, where one round of workgroups covers the output:
+//    gemm_mid.hip, whose workgroups hold up to 256 token rows against 16-128 weight rows;
 //  - otherwise the two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8
 //    on 32x32x32 MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
 #include "common.h"

@@ -97,9 +97,10 @@ hipError_t launch_smooth_scales(const float* a, const float* w, int64_t K, float
 hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float* s, int mode,
                                void* out, hipStream_t st);
 
-// Narrow output tiles sized to the token count (16-128 token rows x 64 or 128 weight rows,
-// 4 waves, K steps through an LDS ring): where it measured faster than the other few-token
-// and mid-size kernels (use_gemm_narrow).
+// Narrow output tiles sized to the token count (16-128 token rows x 16-128 weight rows, 4
+// waves, K through an LDS ring of row-contiguous stages): 2-128 tokens (but 65-128 on
+// 4097-8192 outputs) and 256-512 tokens where one round of 128 x 64 tiles covers the output
+// (use_gemm_narrow).
 bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
 // One token, K a multiple of 1024 up to 16384: whole weight rows per wave on the vector unit
 // (gemm_gemv.hip).

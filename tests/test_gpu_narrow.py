@@ -49,13 +49,18 @@ def _check(y, o, fmt, what):
         assert ok, f"{what}: worst error / bound = {worst:.3f}"
 
 
-# Every tile shape the kernel has (token rows 16 / 32 / 64 / 128, weight rows 64 / 128),
-# ragged M and N (N not a multiple of 4 or 16), one K step, K step counts below and above
-# the ring depth, several row tiles (257-512 tokens), and K = 14336.
-CASES = [(1, 6144, 4096), (16, 4100, 128), (7, 14336, 640), (3, 28672, 256), (17, 5000, 1152),
-         (32, 14336, 384), (32, 20000, 256), (33, 6144, 512), (64, 4099, 2048), (50, 28672, 256),
-         (65, 8200, 640), (128, 14336, 1024), (100, 20000, 256), (128, 28672, 128), (256, 4096, 384),
-         (300, 4101, 256), (512, 4096, 1152), (257, 6144, 128), (384, 4096, 14336)]
+# Every tile the kernel has: 16 x 16 (4-way K split over the waves), 16 x 32 (2-way),
+# 16 x 64 and 32 x 64 on 256- and 512-byte stages, and the 128-byte-step tiles (16 / 32 /
+# 64 / 128 token rows x 64 / 128 weight rows); ragged M and N (N not a multiple of 4 or 16);
+# K a whole number of stages, and K ending in a partial stage (fewer K steps than a stage
+# holds: one, or fewer than the waves splitting it), including K shorter than one stage;
+# step counts below and above the ring depth; several row tiles (257-512 tokens); K = 14336.
+CASES = [(1, 6144, 4096), (5, 4096, 4096), (16, 1000, 640), (9, 3000, 896), (12, 2048, 384),
+         (16, 4100, 128), (7, 14336, 640), (3, 28672, 256), (17, 5000, 1152), (24, 4096, 896),
+         (32, 14336, 384), (32, 20000, 256), (33, 6144, 512), (40, 4096, 4096), (64, 3000, 640),
+         (48, 4096, 1408), (64, 4099, 2048), (50, 28672, 256), (100, 4096, 1152), (65, 8200, 640),
+         (128, 14336, 1024), (100, 20000, 256), (128, 28672, 128), (256, 4096, 384), (300, 4101, 256),
+         (512, 4096, 1152), (257, 6144, 128), (384, 4096, 14336), (16, 4096, 14336), (128, 4096, 14336)]
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
@@ -69,7 +74,8 @@ def test_narrow_parity(M, N, K, fmt):
     _check(y, o, fmt, f"{fmt} {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (64, 28672, 512), (128, 14336, 1024), (512, 4096, 1024)])
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 4096), (8, 4096, 4096), (32, 4096, 896), (64, 28672, 512),
+                                   (128, 14336, 1024), (128, 4096, 4096), (512, 4096, 1024)])
 def test_narrow_repeat_identical(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M + N + K)
