@@ -102,6 +102,11 @@ hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float*
 // 4097-8192 outputs) and 256-512 tokens where one round of 128 x 64 tiles covers the output
 // (use_gemm_narrow).
 bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
+// W4A16, 9-32 tokens (9-16 only on 8193-16384 outputs) with K a multiple of 512: narrow
+// tiles with row-contiguous LDS stages (w4a16_narrow.hip).
+bool use_w4a16_narrow(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_w4a16_narrow(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
+                                    int64_t K, void* y, hipStream_t st);
 // One token, K a multiple of 1024 up to 16384: whole weight rows per wave on the vector unit
 // (gemm_gemv.hip).
 bool use_gemm_gemv(int64_t M, int64_t N, int64_t K);

@@ -337,6 +337,7 @@ hipError_t launch_gemm_w4a16(const void* x, const void* wq, const uint16_t* sc, 
       default: return launch_w4a16_gemv<8>(x, wq, sc, N, K, y, st);
     }
   }
+  if (use_w4a16_narrow(M, N, K)) return launch_gemm_w4a16_narrow(x, wq, sc, M, N, K, y, st);
   if (use_w4a16_mid(M, N, K)) return launch_gemm_w4a16_mid(x, wq, sc, M, N, K, y, st);
   for (int64_t m0 = 0; m0 < M; m0 += 128) {
     const int64_t mr = M - m0 < 128 ? M - m0 : 128;

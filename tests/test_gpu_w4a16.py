@@ -99,6 +99,21 @@ def test_gemm_w4a16_gemv(M, N, K):
     _gemm_compare(xb, wb, f"gemv {M}x{N}x{K}")
 
 
+# 9-32 tokens with K a multiple of 512 take the narrow-tile kernel: 16 x 32 tiles (9-16 tokens
+# above 8192 outputs; 17-32 tokens up to 8192), 16 x 16 tiles (17-32 tokens up to 4096
+# outputs, groups split over 4 waves) and 32 x 64 tiles (17-32 tokens up to 16384); ragged M
+# and N, one stage (K = 512, fewer stages than the ring holds) up to many
+@pytest.mark.parametrize("M,N,K", [(9, 8200, 512), (12, 9001, 2048), (16, 16384, 1536), (17, 100, 512),
+                                   (20, 4099, 1536), (32, 4096, 4096), (24, 6144, 1024), (31, 8191, 512),
+                                   (25, 9000, 1536), (32, 14336, 2048)])
+def test_gemm_w4a16_narrow(M, N, K):
+    need_gpu()
+    rng = np.random.default_rng(M * 11 + N * 7 + K)
+    xb = _bf16(rng.standard_normal((M, K)))
+    wb = _bf16(rng.standard_normal((N, K)) * 0.02)
+    _gemm_compare(xb, wb, f"narrow {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("N", synthetic.DECODE_NS)
 def test_gemm_w4a16_decode_sweep(N):
     """The decode sweep's shapes (M in 1, 8, 32, 128; K = 4096) on its activations."""
