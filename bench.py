@@ -854,16 +854,21 @@ def run_decode(args, c: Ctx):
                 for i in range(max(args.warmup, 3)):
                     quant(i)
                     gemm(i)
+                def lin(i, s=sh):
+                    c.check(L.w8a8_linear(x.data_ptr(), ws[i % copies].data_ptr(), sw.data_ptr(), M, N, K, fmt,
+                                          xq.data_ptr(), sx.data_ptr(), y.data_ptr(), s))
+
                 R = 3 * copies
                 q_us = _graph_mean_s(c, quant, R) * 1e6
                 g_us = _graph_mean_s(c, gemm, R) * 1e6
+                l_us = _graph_mean_s(c, lin, R) * 1e6
                 ge_us = _launch_mean_s(c, gemm, R) * 1e6
                 byt = N * K + M * K + 2 * M * N + 4 * (M + N)
                 flops = 2.0 * M * N * K
                 attain = min(FP8_PEAK_TFLOPS, flops / byt * HBM_PEAK_GBPS / 1e3)   # TFLOP/s
                 cases.append({"M": M, "N": N, "fmt": "fp8" if fmt == 0 else "int8",
                               "gemm_us": round(g_us, 2), "gemm_eager_us": round(ge_us, 2),
-                              "quant_us": round(q_us, 2),
+                              "quant_us": round(q_us, 2), "linear_us": round(l_us, 2),
                               "gemm_GBps": round(byt / g_us / 1e3, 1),
                               "gemm_tflops": round(flops / g_us / 1e6, 2),
                               "roofline_frac": round(flops / g_us / 1e6 / attain, 4)})
@@ -884,8 +889,9 @@ def run_decode(args, c: Ctx):
                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None}
     rec["cases"] = cases
     rec["timing"] = ("per case: 3 x (weight copies) launches over rotating weights captured in one HIP graph "
-                     "and replayed (gemm_us, quant_us); gemm_eager_us: the same launches issued from the "
-                     "host back to back")
+                     "and replayed (gemm_us, quant_us; linear_us: w8a8_linear, the quantizer and the GEMM in one "
+                     "call, one fused kernel for one token); gemm_eager_us: the same GEMM launches issued from "
+                     "the host back to back")
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = decode_cpu_baseline()
     return rec

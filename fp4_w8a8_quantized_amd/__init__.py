@@ -44,6 +44,7 @@ _SIGNATURES = {
     "w8a8_quantize_per_token": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp],
     "w8a8_quantize_weight_per_channel": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp],
+    "w8a8_linear": [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp],
     "w8a8_gemm_ex": [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_int,
                      _c_int, _c_float, _c_vp, _c_vp],
     "w8a8_quantize_static": [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp],
@@ -211,11 +212,30 @@ def gemm_ex(xq: torch.Tensor, sx: torch.Tensor, wq: torch.Tensor, sw: torch.Tens
     return y
 
 
-def linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor) -> torch.Tensor:
-    """W8A8 linear layer: quantize x per token (format of wq), then the scaled GEMM."""
+def linear(x: torch.Tensor, wq: torch.Tensor, sw: torch.Tensor, out=None, xq_out=None, sx_out=None,
+           return_codes: bool = False):
+    """W8A8 linear layer (w8a8_linear): quantize x per token in the format of wq, then the
+    scaled GEMM. Returns y, or (y, xq, sx) with return_codes."""
     fmt = FMT_INT8 if wq.dtype == torch.int8 else FMT_E4M3FN
-    xq, sx = quantize_per_token(x, fmt)
-    return gemm(xq, sx, wq, sw)
+    x = _dev(x, "x", torch.bfloat16, 2)
+    wq = _dev(wq, "wq", wq.dtype, 2)
+    M, K = x.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("x and wq disagree on K")
+    qdt = torch.int8 if fmt == FMT_INT8 else torch.float8_e4m3fn
+    xq = xq_out if xq_out is not None else torch.empty((M, K), dtype=qdt, device=x.device)
+    sx = sx_out if sx_out is not None else torch.empty((M,), dtype=torch.float32, device=x.device)
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _dev(xq, "xq_out", qdt, 2)
+    _dev(sx, "sx_out", torch.float32, 1)
+    _dev(y, "out", torch.bfloat16, 2)
+    if tuple(xq.shape) != (M, K) or tuple(sx.shape) != (M,) or tuple(y.shape) != (M, N):
+        raise ValueError("xq_out must be [M, K], sx_out [M], out [M, N]")
+    _check(lib().w8a8_linear(x.data_ptr(), wq.data_ptr(), _dev(sw, "sw", torch.float32, 1).data_ptr(),
+                             M, N, K, fmt, xq.data_ptr(), sx.data_ptr(), y.data_ptr(), _stream(x)),
+           "w8a8_linear")
+    return (y, xq, sx) if return_codes else y
 
 
 # ------------------------------------------------------------------------------ static scales

@@ -89,6 +89,22 @@ w8a8_status w8a8_gemm(const void* xq, const float* sx, const void* wq, const flo
   return hip_status(w8a8::launch_gemm(xq, sx, wq, sw, M, N, K, fmt, y_bf16, as_stream(stream)));
 }
 
+w8a8_status w8a8_linear(const void* x_bf16, const void* wq, const float* sw, int64_t M, int64_t N,
+                        int64_t K, int fmt, void* xq, float* sx, void* y_bf16, void* stream) {
+  if (fmt != W8A8_FMT_E4M3FN && fmt != W8A8_FMT_INT8) return W8A8_ERR_UNSUPPORTED;
+  w8a8_status st = check_dims(M, K);
+  if (st != W8A8_OK) return st;
+  st = check_gemm(xq, sx, wq, sw, M, N, K, 128, K, y_bf16);
+  if (st != W8A8_OK || M == 0 || N == 0) return st;
+  if (!x_bf16) return W8A8_ERR_NULL;
+  if (!aligned16(x_bf16)) return W8A8_ERR_ALIGN;
+  if (w8a8::use_gemm_gemv(M, N, K))
+    return hip_status(w8a8::launch_linear_gemv(x_bf16, wq, sw, N, K, fmt, xq, sx, y_bf16, as_stream(stream)));
+  const hipError_t e = w8a8::launch_quantize_rows(x_bf16, M, K, fmt, xq, sx, as_stream(stream));
+  if (e != hipSuccess) return W8A8_ERR_HIP;
+  return hip_status(w8a8::launch_gemm(xq, sx, wq, sw, M, N, K, fmt, y_bf16, as_stream(stream)));
+}
+
 w8a8_status w8a8_gemm_ex(const void* xq, const float* sx, const void* wq, const float* sw,
                          int64_t M, int64_t N, int64_t K, int fmt, const void* bias_bf16,
                          int act, int out_fmt, float out_scale, void* y, void* stream) {

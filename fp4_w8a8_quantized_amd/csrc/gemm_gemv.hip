@@ -28,11 +28,16 @@ namespace {
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kGmChunk = 1024;          // K bytes per load of a whole wave
 
-template <int L>
+// FUSED: the kernel also quantizes X. Every workgroup reads the bf16 row (2K bytes) and
+// encodes it into its LDS copy exactly as the per-token quantizer does (row amax, one IEEE
+// division for the scale, the same per-element encode); workgroup 0 also stores the codes
+// and the scale. That replaces the quantizer's launch in a one-token linear layer.
+template <int L, bool FUSED>
 __global__ void __launch_bounds__(256)
 gemm_gemv_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                  const uint8_t* __restrict__ wq, const float* __restrict__ sw, int N, int K,
-                 int kind, void* __restrict__ yp, Epilogue ep) {
+                 int kind, void* __restrict__ yp, Epilogue ep, const uint16_t* __restrict__ xbf,
+                 uint8_t* __restrict__ xq_out, float* __restrict__ sx_out) {
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6), GW = gridDim.x * 4;
   const int cnt = gw < N ? (N - 1 - gw) / GW + 1 : 0;
@@ -45,7 +50,56 @@ gemm_gemv_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   if (cnt > 0) load(0);
 
   __shared__ u32x4 xl[64 * L];
-  for (int c = threadIdx.x; c < 64 * L; c += 256) xl[c] = reinterpret_cast<const u32x4*>(xq)[c];
+  float sxv;
+  if constexpr (FUSED) {
+    // The row's 16-byte chunks of bf16 (128 L of them) stay in registers from the amax to the
+    // encode: chunk threadIdx.x + 256 i is element i of xraw.
+    constexpr int XC = (L + 1) / 2;
+    const u32x4* xr = reinterpret_cast<const u32x4*>(xbf);
+    const int nchunk = K >> 3;
+    u32x4 xraw[XC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      xraw[i] = c < nchunk ? xr[c] : u32x4{0u, 0u, 0u, 0u};
+      amax = fmaxf(amax, chunk_absmax(xraw[i]));
+    }
+    amax = wave_max(amax);
+    __shared__ float red[4];
+    if (lane == 0) red[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = amax_scale(amax, kind == 1 ? 127.0f : 448.0f);
+    const bool finite = __builtin_isfinite(s);
+    const float rcp = 1.0f / s;
+    u32x2* xl2 = reinterpret_cast<u32x2*>(xl);
+#pragma unroll
+    for (int i = 0; i < XC; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      if (c >= nchunk) break;
+      const u32x4 v = xraw[i];
+      float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                    bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = finite ? div_by_scale(f[e], s, rcp) : f[e] / s;
+      u32x2 o;
+      if (kind == 1) {
+        o.x = int8_code(f[0]) | (int8_code(f[1]) << 8) | (int8_code(f[2]) << 16) | (int8_code(f[3]) << 24);
+        o.y = int8_code(f[4]) | (int8_code(f[5]) << 8) | (int8_code(f[6]) << 16) | (int8_code(f[7]) << 24);
+      } else {
+        o.x = pack_e4m3x4(f[0], f[1], f[2], f[3]);
+        o.y = pack_e4m3x4(f[4], f[5], f[6], f[7]);
+      }
+      xl2[c] = o;
+      if (blockIdx.x == 0) reinterpret_cast<u32x2*>(xq_out)[c] = o;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) sx_out[0] = s;
+    sxv = s;
+  } else {
+    for (int c = threadIdx.x; c < 64 * L; c += 256) xl[c] = reinterpret_cast<const u32x4*>(xq)[c];
+    sxv = sx[0];
+  }
   __syncthreads();
   // The lane's X bytes of load slot t: bf16 pairs (FP8) or the raw words (INT8).
   uint32_t xv[L][8];
@@ -64,7 +118,6 @@ gemm_gemv_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
       }
     }
   }
-  const float sxv = sx[0];
 
   for (int i = 0; i < cnt; ++i) {
     float accf = 0.f;
@@ -113,12 +166,12 @@ gemm_gemv_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 // at once (the register count grows with K). Measured at K = 4096: 4096 rows best at 768
 // workgroups (5.0 us against 5.6 at 512), 14336 rows at 2048 (11.0 against 11.4 at 1024);
 // K = 14336 (two waves per SIMD) at the 512 that fit.
-template <int L>
+template <int L, bool FUSED>
 int gemv_blocks(int64_t N) {
   static int resident = 0;                         // per CU x CUs, the same on every call
   if (resident == 0) {
     int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_gemv_kernel<L>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_gemv_kernel<L, FUSED>, 256, 0) != hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 1024;
@@ -131,9 +184,19 @@ int gemv_blocks(int64_t N) {
 template <int L>
 hipError_t launch_l(const void* xq, const float* sx, const void* wq, const float* sw, int64_t N,
                     int64_t K, int fmt, void* y, hipStream_t st, const Epilogue& ep) {
-  const int blocks = gemv_blocks<L>(N);
-  hipLaunchKernelGGL((gemm_gemv_kernel<L>), dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)xq, sx,
-                     (const uint8_t*)wq, sw, (int)N, (int)K, fmt, y, ep);
+  const int blocks = gemv_blocks<L, false>(N);
+  hipLaunchKernelGGL((gemm_gemv_kernel<L, false>), dim3((unsigned)blocks), dim3(256), 0, st, (const uint8_t*)xq, sx,
+                     (const uint8_t*)wq, sw, (int)N, (int)K, fmt, y, ep, nullptr, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+template <int L>
+hipError_t launch_fused_l(const void* xbf, const void* wq, const float* sw, int64_t N, int64_t K, int fmt,
+                          void* xq, float* sx, void* y, hipStream_t st) {
+  const int blocks = gemv_blocks<L, true>(N);
+  hipLaunchKernelGGL((gemm_gemv_kernel<L, true>), dim3((unsigned)blocks), dim3(256), 0, st, nullptr, nullptr,
+                     (const uint8_t*)wq, sw, (int)N, (int)K, fmt, y, Epilogue{}, (const uint16_t*)xbf,
+                     (uint8_t*)xq, sx);
   return hipGetLastError();
 }
 
@@ -162,6 +225,28 @@ hipError_t launch_gemm_gemv(const void* xq, const float* sx, const void* wq, con
     case 14: return launch_l<14>(xq, sx, wq, sw, N, K, fmt, y, st, ep);
     case 15: return launch_l<15>(xq, sx, wq, sw, N, K, fmt, y, st, ep);
     default: return launch_l<16>(xq, sx, wq, sw, N, K, fmt, y, st, ep);
+  }
+}
+
+hipError_t launch_linear_gemv(const void* xbf, const void* wq, const float* sw, int64_t N, int64_t K, int fmt,
+                              void* xq, float* sx, void* y, hipStream_t st) {
+  switch (K / kGmChunk) {
+    case 1: return launch_fused_l<1>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 2: return launch_fused_l<2>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 3: return launch_fused_l<3>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 4: return launch_fused_l<4>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 5: return launch_fused_l<5>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 6: return launch_fused_l<6>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 7: return launch_fused_l<7>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 8: return launch_fused_l<8>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 9: return launch_fused_l<9>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 10: return launch_fused_l<10>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 11: return launch_fused_l<11>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 12: return launch_fused_l<12>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 13: return launch_fused_l<13>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 14: return launch_fused_l<14>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    case 15: return launch_fused_l<15>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
+    default: return launch_fused_l<16>(xbf, wq, sw, N, K, fmt, xq, sx, y, st);
   }
 }
 

@@ -112,6 +112,10 @@ hipError_t launch_gemm_w4a16_narrow(const void* x, const void* wq, const uint16_
 bool use_gemm_gemv(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_gemv(const void* xq, const float* sx, const void* wq, const float* sw, int64_t N,
                             int64_t K, int fmt, void* y, hipStream_t st, const Epilogue& ep);
+// One-token linear layer in one launch: the GEMV kernel quantizes the bf16 row itself (per
+// token, bit-identical to the quantizer) and also stores the codes and the scale.
+hipError_t launch_linear_gemv(const void* xbf, const void* wq, const float* sw, int64_t N, int64_t K, int fmt,
+                              void* xq, float* sx, void* y, hipStream_t st);
 hipError_t launch_gemm_narrow(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                               const Epilogue& ep);

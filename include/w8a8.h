@@ -98,6 +98,24 @@ w8a8_status w8a8_quantize_weight_per_channel(const void* w_bf16, int64_t N, int6
 w8a8_status w8a8_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                       int64_t M, int64_t N, int64_t K, int fmt, void* y_bf16, void* stream);
 
+/* ------------------------------------------------------------------------------------
+ * One W8A8 linear layer on bf16 activations: the per-token quantization of
+ * w8a8_quantize_per_token followed by the scaled GEMM of w8a8_gemm, as the pages run a
+ * quantized linear ([P-FP8FP4] Implementation sketch: fp8_per_token on the activations, the
+ * weights quantized offline, the scaled matrix product; [P-FP8INT8] §6-9 for the GEMM).
+ *   x_bf16 [M, K] bf16 activations (read only);
+ *   wq [N, K] weight codes and sw fp32 [N], from w8a8_quantize_weight_per_channel;
+ *   xq [M, K] codes and sx fp32 [M]: written, exactly what w8a8_quantize_per_token gives;
+ *   y_bf16 [M, N]: written, exactly what w8a8_gemm gives for (xq, sx, wq, sw).
+ * One token (M = 1) with K a multiple of 1024 up to 16384 runs as one kernel that quantizes
+ * the row and computes the GEMM (no quantizer launch); other shapes run the two kernels in
+ * order on the stream. All pointers are device memory owned by the caller, 16-byte aligned;
+ * x must not overlap xq, sx or y. Rules and errors as w8a8_gemm (K a multiple of 128, both
+ * formats), plus those of the quantizer for x; with M = 0 or N = 0 nothing is written.
+ */
+w8a8_status w8a8_linear(const void* x_bf16, const void* wq, const float* sw, int64_t M, int64_t N,
+                        int64_t K, int fmt, void* xq, float* sx, void* y_bf16, void* stream);
+
 typedef enum {
   W8A8_ACT_NONE = 0,        /* identity                                                */
   W8A8_ACT_RELU = 1,        /* max(v, 0)                                               */

@@ -32,6 +32,9 @@ hipError_t launch_quantize_group(const void* x, int64_t M, int64_t K, void*, flo
 hipError_t launch_quantize_block(const void* w, int64_t N, int64_t K, void*, float*, hipStream_t) { return record(w, N, K, 0); }
 hipError_t launch_quantize_mxfp4(const void* x, int64_t R, int64_t K, void*, uint8_t*, hipStream_t) { return record(x, R, K, 0); }
 hipError_t launch_gemm(const void* xq, const float*, const void*, const float*, int64_t M, int64_t N, int64_t K, int, void*, hipStream_t, const Epilogue& ep) { return record(xq, M, N, K + 1000000 * ep.act); }
+hipError_t launch_linear_gemv(const void* x, const void*, const float*, int64_t N, int64_t K, int fmt, void*, float*, void*, hipStream_t) { return record(x, N, K, fmt); }
+// the one-token kernel's shape rule, as the library states it
+bool use_gemm_gemv(int64_t M, int64_t N, int64_t K) { return M == 1 && K % 1024 == 0 && K / 1024 >= 1 && K / 1024 <= 16 && N >= 1; }
 hipError_t launch_gemm_blockscaled(const void* xq, const float*, const void*, const float*, int64_t M, int64_t N, int64_t K, void*, hipStream_t) { return record(xq, M, N, K); }
 hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t*, const void*, const uint8_t*, int64_t M, int64_t N, int64_t K, void*, hipStream_t) { return record(xq, M, N, K); }
 hipError_t launch_quantize_nvfp4(const void* x, int64_t R, int64_t K, bool given, void*, uint8_t*, float*, hipStream_t) { return record(x, R, K, given); }
@@ -106,6 +109,27 @@ int main() {
   CHECK_CALL(w8a8_gemm(A, F, A, F, 5, 7, 256, 0, U, nullptr), W8A8_ERR_ALIGN);
   CHECK_NO_LAUNCH(w8a8_gemm(A, F, A, F, 0, 7, 256, 0, nullptr, nullptr), W8A8_OK);
   CHECK_NO_LAUNCH(w8a8_stream_probe(nullptr, 0, nullptr, nullptr), W8A8_OK);
+  // one linear layer: one fused launch for one token (K a multiple of 1024), else the
+  // quantizer and the GEMM
+  {
+    const int before = g_calls;
+    EXPECT(w8a8_linear(A, A, F, 1, 7, 4096, 0, A, F, A, nullptr) == W8A8_OK);
+    EXPECT(g_calls - before == 1 && g_p == A && g_a == 7 && g_b == 4096 && g_c == 0);
+    EXPECT(w8a8_linear(A, A, F, 5, 7, 256, 1, A, F, A, nullptr) == W8A8_OK);
+    EXPECT(g_calls - before == 3 && g_a == 5 && g_b == 7 && g_c == 256);   // the GEMM came last
+    EXPECT(w8a8_linear(A, A, F, 1, 7, 640, 0, A, F, A, nullptr) == W8A8_OK);
+    EXPECT(g_calls - before == 5);
+  }
+  CHECK_CALL(w8a8_linear(A, A, F, 5, 7, 200, 0, A, F, A, nullptr), W8A8_ERR_UNSUPPORTED);
+  CHECK_CALL(w8a8_linear(A, A, F, 5, 7, 256, 3, A, F, A, nullptr), W8A8_ERR_UNSUPPORTED);
+  CHECK_CALL(w8a8_linear(nullptr, A, F, 5, 7, 256, 0, A, F, A, nullptr), W8A8_ERR_NULL);
+  CHECK_CALL(w8a8_linear(A, A, F, 5, 7, 256, 0, nullptr, F, A, nullptr), W8A8_ERR_NULL);
+  CHECK_CALL(w8a8_linear(U, A, F, 5, 7, 256, 0, A, F, A, nullptr), W8A8_ERR_ALIGN);
+  CHECK_CALL(w8a8_linear(A, A, F, -1, 7, 256, 0, A, F, A, nullptr), W8A8_ERR_SHAPE);
+  CHECK_CALL(w8a8_linear(A, A, F, big, 7, big, 0, A, F, A, nullptr), W8A8_ERR_SHAPE);
+  CHECK_NO_LAUNCH(w8a8_linear(nullptr, nullptr, nullptr, 0, 7, 256, 0, nullptr, nullptr, nullptr, nullptr), W8A8_OK);
+  CHECK_NO_LAUNCH(w8a8_linear(nullptr, nullptr, nullptr, 3, 0, 256, 0, nullptr, nullptr, nullptr, nullptr), W8A8_OK);
+
   CHECK_CALL(w8a8_gemm_ex(A, F, A, F, 5, 7, 256, 1, A, 2, 1, 0.5f, A, nullptr), W8A8_OK);
   EXPECT(g_c == 256 + 2000000);
   CHECK_CALL(w8a8_gemm_ex(A, F, A, F, 5, 7, 256, 0, nullptr, 3, 0, 1.f, A, nullptr), W8A8_ERR_UNSUPPORTED);

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["w8a8_quantize_per_token", "w8a8_quantize_weight_per_channel", "w8a8_gemm", "w8a8_gemm_ex",
+    for n in ["w8a8_quantize_per_token", "w8a8_quantize_weight_per_channel", "w8a8_gemm", "w8a8_linear",
+              "w8a8_gemm_ex",
               "w8a8_quantize_per_token_group", "w8a8_quantize_weight_block", "w8a8_gemm_blockscaled",
               "w8a8_quantize_mxfp4", "w8a8_gemm_mxfp4", "w8a8_channel_absmax",
               "w8a8_smoothquant_scales", "w8a8_smooth_apply", "w8a8_status_string",
@@ -86,6 +87,23 @@ def test_gemm_validation(L):
     assert g(A, A, A, A, 4, 4, 128, 0, MIS, None) == EALIGN
     assert g(None, None, None, None, 0, 4, 128, 0, None, None) == OK
     assert g(None, None, None, None, 4, 0, 128, 1, None, None) == OK
+
+
+def test_linear_validation(L):
+    f = L.w8a8_linear
+    ok = (A, A, A, 4, 4, 128, 0, A, A, A, None)
+    assert f(None, *ok[1:]) == ENULL                                   # x
+    assert f(A, A, A, 4, 4, 128, 0, None, A, A, None) == ENULL         # xq
+    assert f(A, A, A, 4, 4, 128, 0, A, None, A, None) == ENULL         # sx
+    assert f(A, A, A, 4, 4, 128, 0, A, A, None, None) == ENULL         # y
+    assert f(A, A, A, 4, 4, 100, 0, A, A, A, None) == EUNSUP           # K % 128
+    assert f(A, A, A, 4, 4, 128, 2, A, A, A, None) == EUNSUP           # format
+    assert f(A, A, A, -1, 4, 128, 0, A, A, A, None) == ESHAPE
+    assert f(A, A, A, 1 << 40, 4, 1 << 20, 0, A, A, A, None) == ESHAPE
+    assert f(MIS, *ok[1:]) == EALIGN
+    assert f(A, A, A, 4, 4, 128, 0, MIS, A, A, None) == EALIGN
+    assert f(None, None, None, 0, 4, 128, 0, None, None, None, None) == OK
+    assert f(None, None, None, 4, 0, 128, 1, None, None, None, None) == OK
 
 
 def test_gemm_ex_validation(L):
