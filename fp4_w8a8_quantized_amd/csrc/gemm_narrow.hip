@@ -7,16 +7,16 @@
 //
 // Below the ridge point the weights dominate the traffic ("Low-bit LLM Weights and
 // Activations" §5): the kernel's time is the time to stream W from HBM once, plus what the
-// CUs spend re-reading X from the L2. A workgroup of 4 waves owns BM token rows (16-128)
+// CUs spend re-reading X from the L2. A workgroup of 4 or 8 waves owns BM token rows (16-128)
 // against BN weight rows (16-128), a tile picked so that about one round of workgroups
-// covers the output with the fewest bytes per CU:
+// covers the output with the fewest bytes per CU (8 waves on the 64- and 128-row tiles):
 //  - each LDS stage holds KB bytes of K (256-1024; 128 on the largest tiles) of every X and
 //    W row of the tile. A stage is filled by direct-to-LDS loads that each read whole cache
 //    lines of 1024 / KB rows, so the weight stream reaches HBM as runs of KB contiguous bytes
 //    per row rather than one 128-byte line per row per K step;
 //  - a ring of ST stages is issued ST - 1 stages ahead; one barrier per stage publishes it
 //    and retires the one read before;
-//  - the 4 waves form a WM x WN x WK grid: wave (wm, wn, wk) owns a (BM / WM) x (BN / WN)
+//  - the waves form a WM x WN x WK grid: wave (wm, wn, wk) owns a (BM / WM) x (BN / WN)
 //    part of the tile as 16 x 16 subtiles and the K steps s = wk mod WK of every stage. With
 //    WK > 1 (tiles too small for 4 waves) the waves' partial sums meet in LDS after the loop,
 //    added in wk order;
@@ -57,24 +57,24 @@ __device__ __forceinline__ int nw_slot(int r, int c) {
   else return c ^ ((r >> 1) & 7);
 }
 
-template <int KIND, int BM, int BN, int WK, int KB, int ST, bool OF8>
-__global__ void __launch_bounds__(256)
+template <int KIND, int BM, int BN, int WK, int KB, int ST, bool OF8, int NWV>
+__global__ void __launch_bounds__(64 * NWV)
 gemm_narrow_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                    const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
                    int K, int kblocks, int ksteps, int tiles_m, void* __restrict__ yp, Epilogue ep) {
-  constexpr int WMN = 4 / WK;
+  constexpr int WMN = NWV / WK;
   constexpr int WM = (BM >= 32 && WMN >= 2) ? 2 : 1, WN = WMN / WM;
   constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   constexpr int SM = TM / 16, SN = TN / 16;          // 16 x 16 subtiles per wave
-  static_assert(WK * WMN == 4 && SM >= 1 && SN >= 1 && SM * 16 * WM == BM && SN * 16 * WN == BN, "tile shape");
+  static_assert(WK * WMN == NWV && SM >= 1 && SN >= 1 && SM * 16 * WM == BM && SN * 16 * WN == BN, "tile shape");
   constexpr int SPB = KB / 128;                      // K steps per stage
   static_assert(SPB % WK == 0, "every wave takes the same number of steps per stage");
   constexpr int RPL = 1024 / KB, LPR = KB / 16;      // rows per 1 KB load, lanes per row
   constexpr int XST = BM * KB, STAGE = (BM + BN) * KB;
   constexpr int NDX = BM / RPL, ND = (BM + BN) / RPL;   // 1 KB loads per stage
   static_assert(BM % RPL == 0 && BN % RPL == 0, "whole rows per load");
-  constexpr int NQ = (ND + 3) / 4;                   // loads per wave per stage, at most
-  constexpr int NDR = ND % 4;                        // waves below NDR issue NQ, others NQ - 1
+  constexpr int NQ = (ND + NWV - 1) / NWV;           // loads per wave per stage, at most
+  constexpr int NDR = ND % NWV;                      // waves below NDR issue NQ, others NQ - 1
   constexpr int LA = NQ, LB = NDR == 0 ? NQ : NQ - 1;
   static_assert(ST >= 3 && LA * (ST - 2) < 64, "vmcnt holds at most 63");
   static_assert(ST * STAGE <= 160 * 1024, "LDS");
@@ -116,7 +116,7 @@ gemm_narrow_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   uint32_t vrow[NQ], vchunk[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
-    const int d = min(wave + 4 * q, ND - 1);
+    const int d = min(wave + NWV * q, ND - 1);
     const bool isx = d < NDX;
     const int r = RPL * (isx ? d : d - NDX) + lrow;
     const int row = isx ? min(m0 + r, M - 1) : min(n0 + r, N - 1);
@@ -127,7 +127,7 @@ gemm_narrow_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     const uint32_t sb = lds0 + (kb % ST) * STAGE;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int d = wave + 4 * q;
+      const int d = wave + NWV * q;
       if (d < ND) {
         const bool isx = d < NDX;
         const uint32_t la = sb + (isx ? 0 : XST) + (isx ? d : d - NDX) * 1024;
@@ -285,45 +285,49 @@ gemm_narrow_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   });
 }
 
-template <int KIND, int BM, int BN, int WK, int KB, int ST>
+template <int KIND, int BM, int BN, int WK, int KB, int ST, int NWV>
 hipError_t launch_nw(const void* xq, const float* sx, const void* wq, const float* sw, int64_t M,
                      int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles = tiles_m * (int)((N + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(256);
+  const dim3 grid((unsigned)tiles), block(64 * NWV);
   const int kblocks = (int)((K + KB - 1) / KB), ksteps = (int)(K / 128);
   if (ep.out_fp8)
-    hipLaunchKernelGGL((gemm_narrow_kernel<KIND, BM, BN, WK, KB, ST, true>), grid, block, 0, st, (const uint8_t*)xq, sx,
+    hipLaunchKernelGGL((gemm_narrow_kernel<KIND, BM, BN, WK, KB, ST, true, NWV>), grid, block, 0, st, (const uint8_t*)xq, sx,
                        (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, kblocks, ksteps, tiles_m, y, ep);
   else
-    hipLaunchKernelGGL((gemm_narrow_kernel<KIND, BM, BN, WK, KB, ST, false>), grid, block, 0, st, (const uint8_t*)xq, sx,
+    hipLaunchKernelGGL((gemm_narrow_kernel<KIND, BM, BN, WK, KB, ST, false, NWV>), grid, block, 0, st, (const uint8_t*)xq, sx,
                        (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, kblocks, ksteps, tiles_m, y, ep);
   return hipGetLastError();
 }
 
-// The tiles, with the stage depth that measured best for each (FP8, K = 4096; LDS per
-// workgroup in brackets, two workgroups share a CU up to 80 KB):
-//   0  16 x 16,  WK 4, 512-byte stages x 4  [64 KB]
-//   1  16 x 32,  WK 2, 512 x 3              [72 KB]
-//   2  16 x 64,  256 x 4                    [80 KB]
-//   3  32 x 64,  512 x 3                    [144 KB]
-//   4.. the 128-byte-step tiles (16 | 32 | 64 | 128) x (64 | 128).
+// The tiles, with the stage depth and wave count that measured best for each (FP8, K = 4096;
+// LDS per workgroup in brackets, two workgroups share a CU up to 80 KB):
+//   0  16 x 16,  4 waves splitting K 4 ways, 512-byte stages x 4  [64 KB]
+//   1  16 x 32,  4 waves splitting K 2 ways, 512 x 3              [72 KB]
+//   2  16 x 64,  4 waves, 256 x 4                                 [80 KB]
+//   3  32 x 64,  4 waves, 512 x 3                                 [144 KB]
+//   4-7  (16 | 32) x (64 | 128) on 128-byte steps, 4 waves
+//   8-11 (64 | 128) x (64 | 128), 8 waves: 8 waves issue twice the loads at once, which
+//     measured 5-13% faster than 4 on these tiles (512 x 4096 18.4 -> 16.7 us, 48 x 14336
+//     16.4 -> 14.9, 384 x 4096 x 14336 52.0 -> 46.4, 100 x 20000 29.0 -> 25.3); on the
+//     32 x 64 tile they made no difference.
 template <int KIND>
 hipError_t launch_nw_cfg(int c, const void* xq, const float* sx, const void* wq, const float* sw,
                          int64_t M, int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
   switch (c) {
-    case 0: return launch_nw<KIND, 16, 16, 4, 512, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 1: return launch_nw<KIND, 16, 32, 2, 512, 3>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 2: return launch_nw<KIND, 16, 64, 1, 256, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 3: return launch_nw<KIND, 32, 64, 1, 512, 3>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 4: return launch_nw<KIND, 16, 64, 1, 128, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 5: return launch_nw<KIND, 16, 128, 1, 128, 6>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 6: return launch_nw<KIND, 32, 64, 1, 128, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 7: return launch_nw<KIND, 32, 128, 1, 128, 5>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 8: return launch_nw<KIND, 64, 64, 1, 128, 6>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 9: return launch_nw<KIND, 64, 128, 1, 128, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 10: return launch_nw<KIND, 128, 64, 1, 128, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    case 11: return launch_nw<KIND, 128, 128, 1, 128, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 0: return launch_nw<KIND, 16, 16, 4, 512, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 1: return launch_nw<KIND, 16, 32, 2, 512, 3, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 2: return launch_nw<KIND, 16, 64, 1, 256, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 3: return launch_nw<KIND, 32, 64, 1, 512, 3, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 4: return launch_nw<KIND, 16, 64, 1, 128, 8, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 5: return launch_nw<KIND, 16, 128, 1, 128, 6, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 6: return launch_nw<KIND, 32, 64, 1, 128, 8, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 7: return launch_nw<KIND, 32, 128, 1, 128, 5, 4>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 8: return launch_nw<KIND, 64, 64, 1, 256, 4, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 9: return launch_nw<KIND, 64, 128, 1, 128, 4, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 10: return launch_nw<KIND, 128, 64, 1, 256, 3, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 11: return launch_nw<KIND, 128, 128, 1, 128, 4, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
     default: return hipErrorInvalidValue;
   }
 }
