@@ -9,14 +9,11 @@
 // Dispatch by shape:
 //  - one token (K a multiple of 1024 up to 16384): whole weight rows per wave on the vector
 //    unit (gemm_gemv.hip);
-//  - 2-128 tokens, and 256-512 tokens where one round of 128 x 64 tiles covers the output:
-//    narrow tiles sized to the token count (gemm_narrow.hip), except 65-128 tokens on
-//    4097-8192 outputs;
+//  - 2-128 tokens, and 129-512 tokens where one round of 128 x 64 or 128 x 128 tiles covers
+//    the output: narrow tiles sized to the token count (gemm_narrow.hip);
 //  - one token that the vector kernel does not take: the weight-streaming split-K kernel
 //    (gemm_skinny.hip);
-//  - otherwise up to 512 tokens, where one round of workgroups covers the output:
-//    gemm_mid.hip, whose workgroups hold up to 256 token rows against 16-128 weight rows;
-//  - otherwise the two-waves-per-SIMD kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8
+//  - otherwise the prefill kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8
 //    on 32x32x32 MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
 #include "common.h"
 #include "internal.h"
@@ -29,8 +26,6 @@ hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const fl
   if (use_gemm_gemv(M, N, K)) return launch_gemm_gemv(xq, sx, wq, sw, N, K, fmt, y, st, ep);
   if (use_gemm_narrow(M, N, K)) return launch_gemm_narrow(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (M <= 32) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
-  if (M <= 512 && mid_weight_rows(M, N) != 0)
-    return launch_gemm_mid(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
   return launch_gemm_int8_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
 }

@@ -336,19 +336,20 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-// Tile for M x N (-1: the kernel does not take the shape). 2-128 tokens: the smallest tile
-// whose workgroups fit one round of the CUs (two per CU for the tiles of up to 80 KB), as
-// measured on MI355X (FP8, graph replay, against the kernels used before: the weight-
-// streaming split-K kernel up to 32 tokens, the mid-size kernel above, the 128-byte-step
-// narrow tiles on wide layers):
+// Tile for M x N (-1: the kernel does not take the shape). The smallest tile whose
+// workgroups fit one round of the CUs (two per CU for the tiles of up to 80 KB), as measured
+// on MI355X (FP8, graph replay, against the kernels used before: the weight-streaming split-K
+// kernel up to 32 tokens, the mid-size kernel above, the 128-byte-step narrow tiles on wide
+// layers):
 //   K = 4096:  8 x 4096 6.6 -> 5.6 us, 32 x 4096 9.2 -> 6.8, 64 x 4096 11.4 -> 8.7,
 //              128 x 4096 12.9 -> 9.9, 16 x 6144 10.1 -> 7.5, 64 x 6144 13.6 -> 10.4,
-//              8 x 14336 14.0 -> 12.8, 32 x 14336 15.2 -> 14.1;
-//   K = 14336: 16 x 4096 20.4 -> 13.0 us, 32 x 4096 27.2 -> 16.9, 128 x 4096 35.9 -> 26.3.
-// 65-128 tokens on 4097-8192 outputs stay on the mid-size kernel (192-256 workgroups;
-// 100 x 6144 14.7 us against 16.4 here). Wider layers take the 128-byte-step tiles, 64
-// weight rows or 128 where 64 would need a second round. 256-512 tokens: 128 x 64 tiles
-// where one round of them covers the output.
+//              100 x 6144 14.8 -> 11.5, 128 x 8192 16.9 -> 13.3, 8 x 14336 14.0 -> 12.8,
+//              32 x 14336 15.2 -> 14.1, 200 x 4096 16.5 -> 15.9, 160 x 6144 18.4 -> 16.3,
+//              384 x 6144 23.6 -> 23.0, 512 x 8192 26.8 -> 24.3;
+//   K = 14336: 16 x 4096 20.4 -> 13.0 us, 32 x 4096 27.2 -> 16.9, 128 x 4096 35.9 -> 26.3,
+//              192 x 4096 48.7 -> 45.9.
+// Wider layers take 64 or 128 weight rows, 128 where 64 would need a second round; above
+// 128 tokens, 128 x 64 or 128 x 128 tiles where one round of them covers the output.
 int narrow_config(int64_t M, int64_t N) {
   if (M < 2 || N < 1) return -1;
   if (M <= 16) {
@@ -368,10 +369,13 @@ int narrow_config(int64_t M, int64_t N) {
   }
   if (M <= 128) {
     if (4 * cdiv(N, 64) <= 256) return 3;
-    if (N <= 8192) return -1;                        // the mid-size kernel's 192-256 workgroups
+    if (2 * cdiv(N, 64) <= 256) return 8;
     return cdiv(N, 64) <= 256 ? 10 : 11;
   }
-  if (M >= 256 && M <= 512 && cdiv(M, 128) * cdiv(N, 64) <= 256) return 10;
+  if (M <= 512) {
+    if (cdiv(M, 128) * cdiv(N, 64) <= 256) return 10;
+    if (cdiv(M, 128) * cdiv(N, 128) <= 256) return 11;
+  }
   return -1;
 }
 

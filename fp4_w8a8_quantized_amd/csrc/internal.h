@@ -46,16 +46,8 @@ hipError_t launch_gemm_solo(const void* xq, const float* sx, const void* wq, con
                             int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                             const Epilogue& ep);
 
-// 33-512 tokens: up to 256 token rows and 16-128 weight rows per workgroup of 4 or 8
-// waves; weights staged in LDS a ring (16 or 8 K steps) ahead, X two or three steps ahead.
-// Weight rows per workgroup of launch_gemm_mid for an M x N output (16, 32, 64, or 128 up
-// to 128 tokens), or 0 if even the widest would take more than one round of workgroups.
-int mid_weight_rows(int64_t M, int64_t N);
-hipError_t launch_gemm_mid(const void* xq, const float* sx, const void* wq, const float* sw,
-                           int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
-                           const Epilogue& ep);
-// Up to 32 tokens (64 on layers too wide for one round of the 33-512-token kernel):
-// weights streamed by 16-, 32- or 64-row workgroups that split K among their waves.
+// One token where the vector kernel does not take K: weights streamed by 16-row workgroups
+// that split K among their waves.
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                               const Epilogue& ep);
@@ -97,10 +89,9 @@ hipError_t launch_smooth_scales(const float* a, const float* w, int64_t K, float
 hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float* s, int mode,
                                void* out, hipStream_t st);
 
-// Narrow output tiles sized to the token count (16-128 token rows x 16-128 weight rows, 4
-// waves, K through an LDS ring of row-contiguous stages): 2-128 tokens (but 65-128 on
-// 4097-8192 outputs) and 256-512 tokens where one round of 128 x 64 tiles covers the output
-// (use_gemm_narrow).
+// Narrow output tiles sized to the token count (16-128 token rows x 16-128 weight rows, 4 or
+// 8 waves, K through an LDS ring of row-contiguous stages): 2-128 tokens, and 129-512 tokens
+// where one round of 128 x 64 or 128 x 128 tiles covers the output (use_gemm_narrow).
 bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
 // W4A16, 9-32 tokens (9-16 only on 8193-16384 outputs) with K a multiple of 512: narrow
 // tiles with row-contiguous LDS stages (w4a16_narrow.hip).

@@ -66,16 +66,12 @@ def test_fp8_ragged(M, N, K):
     _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
 
 
-# Few-token paths (M <= 32, and up to 64 above one round of the next kernel: the
-# weight-streaming kernel; 33 <= M <= 512: the kernel that
-# stages up to 256 token rows and 16-128 weight rows per workgroup): every 16-row bucket
-# edge, N not a multiple of 4 or 16, one K step (most waves idle; the weight ring then
-# re-fetches the only step), K step counts below and above the ring depth, wide layers
-# with a ragged last workgroup (16, 32, 64 and, up to 128 tokens above 16384 outputs, 128
-# weight rows per workgroup), the 8-wave form (129-512 tokens, one or two rows of
-# workgroups), and the tiled kernel where one round of workgroups cannot cover the output
-# (M = 513, 200 tokens on 20000 outputs, or 128 tokens above 32768).
-SKINNY_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (65, 100, 2048),
+# Few-token and mid-size paths (2-512 tokens, the narrow-tile kernel): every tile and several
+# row tiles, every 16-row bucket edge, N not a multiple of 4 or 16, one K step and K ending in
+# a partial stage, step counts below and above the ring depth, wide layers with a ragged last
+# tile (up to 128 weight rows per tile), and the prefill kernels where narrow tiles would take
+# more than one round of the CUs (513 tokens, 200 tokens on 20000 outputs, 400 on 7000).
+FEW_TOKEN_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (65, 100, 2048),
                 (128, 130, 1152), (129, 257, 256), (2, 18, 14336), (16, 9000, 256),
                 (32, 8200, 384), (64, 10000, 1152), (128, 8193, 640), (97, 8209, 128),
                 (111, 4097, 2176), (128, 14336, 384), (200, 4100, 640), (256, 9000, 1152),
@@ -107,7 +103,7 @@ def test_int8_one_token(M, N, K):
     _int8_chain(xb, xcal, wb, 0.5, f"{M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,N,K", SKINNY_CASES)
+@pytest.mark.parametrize("M,N,K", FEW_TOKEN_CASES)
 def test_fp8_few_tokens(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, 11 * M + 5 * N + K)
@@ -250,7 +246,7 @@ def test_int8_repeat_identical(M, N, K):
     assert np.array_equal(gy, oy), f"{M}x{N}x{K}: " + first_mismatch(gy, oy)
 
 
-@pytest.mark.parametrize("M,N,K", SKINNY_CASES)
+@pytest.mark.parametrize("M,N,K", FEW_TOKEN_CASES)
 def test_int8_few_tokens(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, 13 * M + 3 * N + K)

@@ -54,9 +54,9 @@ def _check_tol(y, y_ref, what):
 
 @pytest.mark.parametrize("M", [16, 100, 200, 300])
 def test_fp8_weight_at_limit(raw, M):
-    """W 131072 x 16384 E4M3FN: the few-token kernel at M = 16, the 65-512-token kernel at
-    100 (4 waves) and 200 (8 waves), the prefill kernel at 300 (two rows of the mid-size
-    kernel's workgroups would not fit one round on 131072 outputs)."""
+    """W 131072 x 16384 E4M3FN: the narrow-tile kernel at M = 16 (16 x 128 tiles) and 100
+    (128 x 128 tiles, eight waves), the prefill kernels at 200 and 300 (narrow tiles would
+    take several rounds of the CUs on 131072 outputs)."""
     need_gpu()
     N, K = 131072, 16384
     rng = _rng(1)
