@@ -25,7 +25,7 @@ hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const fl
                        const Epilogue& ep) {
   if (use_gemm_gemv(M, N, K)) return launch_gemm_gemv(xq, sx, wq, sw, N, K, fmt, y, st, ep);
   if (use_gemm_narrow(M, N, K)) return launch_gemm_narrow(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
-  if (M <= 32) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  if (M == 1) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
   return launch_gemm_int8_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
 }

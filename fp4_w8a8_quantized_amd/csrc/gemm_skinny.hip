@@ -1,4 +1,5 @@
-// Few-token W8A8 GEMM (decode: M <= 64) on gfx950: the same result as the tiled GEMM,
+// Few-token W8A8 GEMM (one token, where K does not suit the vector kernel) on gfx950: the same
+// result as the tiled GEMM,
 // y = bf16( s_x[m] s_w[n] sum_k dec(xq) dec(wq) ) for FP8 and
 // y = bf16( fp32(fp32(acc_i32) s_x[m]) s_w[n] ) for INT8, but organised around streaming
 // the weights once at HBM rate.
@@ -9,7 +10,7 @@
 // roofline of batch size). The kernel therefore spreads W over as many CUs and as many
 // loads in flight as possible:
 //  - one workgroup per 16 NW weight rows (NW = 1 at N = 4096: 256 workgroups, one per
-//    CU; wider layers take 32 or 64 rows so that X is re-read fewer times);
+//    CU; wider layers take 32 rows so that X is re-read fewer times);
 //  - its WPB waves split K: wave w takes K steps w, w + WPB, ...; each wave keeps the
 //    weights of the next 4 steps (2 KB each) and the X fragments of the next step in
 //    flight while it computes;
@@ -193,25 +194,17 @@ static hipError_t launch_cfg(const void* xq, const float* sx, const void* wq, co
   return hipGetLastError();
 }
 
-// Shape of the launch by token count (MT 16-row subtiles) and width. Every workgroup
-// re-reads all of X, so wide layers take 32 or 64 weight rows per workgroup once there
-// are enough rows to keep every CU busy; narrow ones keep 16 rows (256 workgroups at
-// N = 4096). Chosen from a sweep on MI355X at K = 4096, N in {4096, 14336}.
+// One token (the dispatcher sends this kernel only the one-token shapes whose K the vector
+// kernel does not take): one 16-row subtile of M, 8 waves splitting K; wide layers take 32
+// weight rows per workgroup so that X is re-read fewer times (a sweep on MI355X at K = 4096,
+// N in {4096, 14336}).
 template <int KIND>
 static hipError_t launch_kind(const void* xq, const float* sx, const void* wq, const float* sw,
                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
                               const Epilogue& ep) {
-  const bool wide = N > 8192;
-  if (M <= 16) {
-    return wide ? launch_cfg<KIND, 1, 8, 2>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                : launch_cfg<KIND, 1, 8, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  }
-  if (M <= 32) {
-    return wide ? launch_cfg<KIND, 2, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                : launch_cfg<KIND, 2, 8, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  }
-  return wide ? launch_cfg<KIND, 4, 4, 4>(xq, sx, wq, sw, M, N, K, y, st, ep)     // M <= 64
-              : launch_cfg<KIND, 4, 4, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  if (M > 16) return hipErrorInvalidValue;
+  return N > 8192 ? launch_cfg<KIND, 1, 8, 2>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                  : launch_cfg<KIND, 1, 8, 1>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 hipError_t launch_gemm_skinny(const void* xq, const float* sx, const void* wq, const float* sw,
