@@ -93,8 +93,9 @@ hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float*
 // 8 waves, K through an LDS ring of row-contiguous stages): 2-128 tokens, and 129-512 tokens
 // where one round of 128 x 64 or 128 x 128 tiles covers the output (use_gemm_narrow).
 bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
-// W4A16, 9-32 tokens (9-16 only on 8193-16384 outputs) with K a multiple of 512: narrow
-// tiles with row-contiguous LDS stages (w4a16_narrow.hip).
+// W4A16, 9-128 tokens with K a multiple of 512 where one round of its tiles covers the output
+// (9-16 tokens only on 8193-16384 outputs): narrow tiles with row-contiguous LDS stages
+// (w4a16_narrow.hip).
 bool use_w4a16_narrow(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w4a16_narrow(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N,
                                     int64_t K, void* y, hipStream_t st);

@@ -1,4 +1,4 @@
-// W4A16 GEMM for 9-32 tokens on gfx950: y = X W^T with bf16 X and symmetric INT4 weights,
+// W4A16 GEMM for 9-128 tokens on gfx950: y = X W^T with bf16 X and symmetric INT4 weights,
 // one fp16 scale per row and group of 128 along K ("Low-bit LLM Weights and Activations"
 // §2.3 for the format, §3.3 for dequantizing the weights next to a 16-bit matrix product).
 // Per group, four 16x16x32 bf16 MFMAs from zero sum the exact products of the activations and
@@ -279,15 +279,24 @@ int64_t w4n_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   9-16 tokens on 8193-16384 outputs: 16 x 32 (8 x 14336 14.0 -> 12.5 us, 16 x 14336
 //     16.0 -> 12.8);
 //   17-32 tokens: 16 x 16 up to 4096 outputs (32 x 4096 11.0 -> 8.8 us), 16 x 32 up to
-//     8192 (24 x 6144 16.8 -> 12.1), 32 x 64 up to 16384 (32 x 14336 25.6 -> 19.6).
+//     8192 (24 x 6144 16.8 -> 12.1), 32 x 64 up to 16384 (32 x 14336 25.6 -> 19.6);
+//   33-64 tokens: 16 x 32 where one round of them (two per CU) covers the output (64 x 4096
+//     17.5 -> 12.6 us, 48 x 4096 17.2 -> 12.3);
+//   65-128 tokens: 32 x 64 where one round covers the output (128 x 4096 20.1 -> 18.9 us).
+// On wider layers above 32 tokens the LDS-staged kernel stays faster (64 x 14336: 30.4
+// against 36.7 us here).
 // Up to 16 tokens on narrower layers the decode kernel stays faster (8 x 4096: 6.3 against
 // 7.2 us): its 8 waves per workgroup hide the load latency that this kernel's stages expose.
 int w4a16_narrow_config(int64_t M, int64_t N, int64_t K) {
-  if (M < 2 || M > 32 || N < 1 || K % 512 != 0) return -1;
+  if (M < 2 || M > 128 || N < 1 || K % 512 != 0) return -1;
   if (M <= 16) return (N > 8192 && w4n_cdiv(N, 32) <= 512) ? 1 : -1;
-  if (2 * w4n_cdiv(N, 16) <= 512) return 0;
-  if (2 * w4n_cdiv(N, 32) <= 512) return 1;
-  return w4n_cdiv(N, 64) <= 256 ? 2 : -1;
+  if (M <= 32) {
+    if (2 * w4n_cdiv(N, 16) <= 512) return 0;
+    if (2 * w4n_cdiv(N, 32) <= 512) return 1;
+    return w4n_cdiv(N, 64) <= 256 ? 2 : -1;
+  }
+  if (M <= 64) return w4n_cdiv(M, 16) * w4n_cdiv(N, 32) <= 512 ? 1 : -1;
+  return w4n_cdiv(M, 32) * w4n_cdiv(N, 64) <= 256 ? 2 : -1;
 }
 
 bool use_w4a16_narrow(int64_t M, int64_t N, int64_t K) { return w4a16_narrow_config(M, N, K) >= 0; }
