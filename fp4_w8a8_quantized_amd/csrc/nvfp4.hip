@@ -29,14 +29,16 @@ __device__ __forceinline__ float nv_tensor_scale(float amax) {
 
 // ------------------------------------------------------------------------- quantization
 // The tensor amax is accumulated, as fp32 bits (non-negative floats order like their
-// bits), in the caller's g slot; the last launch turns it into g.
+// bits), in the caller's g slot; the last launch turns it into g. Both passes over X read it
+// with ordinary loads, so that the second finds much of it in the last-level cache
+// (8192 x 8192: 77-79 -> 74 us for the four launches, against non-temporal loads).
 __global__ void nv_amax_init(uint32_t* slot) { *slot = 0u; }
 
 __global__ __launch_bounds__(256) void nv_amax_kernel(const u32x4* __restrict__ x, int64_t nchunk,
                                                       uint32_t* slot) {
   float m = 0.f;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunk; c += (int64_t)gridDim.x * 256)
-    m = fmaxf(m, chunk_absmax(__builtin_nontemporal_load(x + c)));
+    m = fmaxf(m, chunk_absmax(x[c]));
   m = wave_max(m);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -60,8 +62,8 @@ __global__ __launch_bounds__(256) void nv_quant_kernel(const u32x4* __restrict__
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblk) return;
   const float g = GIVEN ? __uint_as_float(*gp) : nv_tensor_scale(__uint_as_float(*gp));
-  const u32x4 v0 = __builtin_nontemporal_load(x + 2 * b);
-  const u32x4 v1 = __builtin_nontemporal_load(x + 2 * b + 1);
+  const u32x4 v0 = x[2 * b];
+  const u32x4 v1 = x[2 * b + 1];
   const float amax = fmaxf(chunk_absmax(v0), chunk_absmax(v1));
   const float t = (amax / 6.0f) / g;                       // two IEEE divisions, in order
   const uint32_t code = pack_e4m3x4(clamp448(t), 0.f, 0.f, 0.f) & 0xFFu;
