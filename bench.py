@@ -654,7 +654,9 @@ def run_qsweep(args, c: Ctx):
                 del x
             q = torch.empty((M, K), dtype=torch.float8_e4m3fn, device=c.dev)
             sx = torch.empty((M,), dtype=torch.float32, device=c.dev)
-            scale = torch.tensor([float(xs[0].float().abs().max()) / 448.0], dtype=torch.float32, device=c.dev)
+            # the static scale calibrated on every copy, so that nothing saturates: the codec alone
+            scale = torch.tensor([max(float(xc.abs().max().float()) for xc in xs) / 448.0],
+                                 dtype=torch.float32, device=c.dev)
             sat = torch.zeros((1,), dtype=torch.int32, device=c.dev)
             amax = torch.zeros((1,), dtype=torch.float32, device=c.dev)
             reps = 3 * copies

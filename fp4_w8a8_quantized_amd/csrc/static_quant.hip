@@ -18,14 +18,23 @@
 // is one. Other scales divide per element. Counter and maximum are reduced per block and reach memory
 // through at most one vector-memory atomic each per block.
 //
-// Layout of the work: each thread encodes four 16-byte chunks whose loads are all issued
-// first, one block per 1024 chunks (measured on 2048 x 4096 and up: within 1-9% of the
-// per-token quantizer when nothing saturates). Variants that did worse: a grid capped at
-// 1024 blocks looping over one chunk per thread (2.5 against 2.9 TB/s), a grid capped at
-// 512 blocks prefetching its next tile, 1024-thread blocks, eight chunks per thread, and an
-// unconditional atomic maximum per block (20 us instead of 6 on 2048 x 4096: atomics on one
-// address serialize). When every block saturates, its count atomic costs about 2 us per
-// call at 2048 x 4096.
+// Arithmetic: a chunk of eight elements takes the clamp and the saturation count only when
+// its largest magnitude saturates (the quotient is monotone in |x|); every other chunk costs
+// what the per-token quantizer's encode costs. Before that split the kernel ran 8-15% behind
+// the per-token quantizer on the same bytes.
+//
+// Layout of the work: each thread encodes two or four 16-byte chunks whose loads are all
+// issued first, 256 threads a block. Measured, X read from HBM: 6.6 us at 2048 x 4096 and
+// 16.9 us at 2048 x 14336, against 6.8 and 17.6 us for the per-token quantizer; 33.7 us at
+// 16384 x 4096 (equal). Variants that did worse: a grid capped at 1024 blocks looping over one
+// chunk per thread, a grid capped at 512 blocks prefetching its next tile, 1024-thread blocks,
+// eight chunks per thread, ordinary loads, and an unconditional atomic maximum per block
+// (20 us instead of 6 on 2048 x 4096).
+//
+// Atomics on one address serialize at about 5 ns each. Each block that saturated something
+// adds its count with one atomic, and that is the whole cost of saturation: about 1 us per
+// 200 saturating blocks (2048 x 4096 with 200 saturated elements: 7.7 against 6.6 us).
+// Reordering the block's atomics, or issuing them at agent scope, did not change it.
 #include <type_traits>
 
 #include "common.h"
@@ -33,7 +42,7 @@
 
 namespace w8a8 {
 
-template <bool INT8>
+template <bool INT8, int CH, bool NTL, bool NTS>
 __global__ __launch_bounds__(256) void quant_static_kernel(const u32x4* __restrict__ x,
                                                            int64_t nchunks,
                                                            const float* __restrict__ scale,
@@ -47,44 +56,56 @@ __global__ __launch_bounds__(256) void quant_static_kernel(const u32x4* __restri
   const bool shortcut = s >= 0x1p-60f && s <= 0x1p60f;
   uint32_t sat = 0;
   float amax = 0.0f;
-  // Thread t of block b owns the chunks b * 1024 + t + 256 i, i < 4: all four loads are
-  // issued before the first is encoded, so each thread keeps 64 bytes in flight.
-  const int64_t c0 = (int64_t)blockIdx.x * 1024 + threadIdx.x;
-  u32x4 v[4];
+  // Thread t of block b owns the chunks b * 256 * CH + t + 256 i, i < CH: all CH loads are
+  // issued before the first is encoded.
+  const int64_t c0 = (int64_t)blockIdx.x * (256 * CH) + threadIdx.x;
+  u32x4 v[CH];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v[i] = (c0 + 256 * i < nchunks) ? __builtin_nontemporal_load(x + c0 + 256 * i) : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = c0 + 256 * i;
+    v[i] = c < nchunks ? (NTL ? __builtin_nontemporal_load(x + c) : x[c]) : u32x4{0u, 0u, 0u, 0u};
+  }
   auto run = [&](auto fast) {
+    constexpr bool F = decltype(fast)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < CH; ++i) {
       const int64_t c = c0 + 256 * i;
       if (c >= nchunks) break;
-      amax = fmaxf(amax, chunk_absmax(v[i]));
+      // The quotient is monotone in |x|, so an element of the chunk saturates exactly when
+      // the chunk's largest magnitude does. Chunks that do not saturate (almost all of
+      // them) skip the clamp and the count; their quotients cannot overflow either.
+      const float cm = chunk_absmax(v[i]);
+      amax = fmaxf(amax, cm);
+      const float qm = F ? div_static(cm, s, rcp) : cm / s;
+      const bool clips = INT8 ? __builtin_rintf(qm) > 127.0f : qm > 448.0f;
       float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
                     bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+      if (!clips) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = decltype(fast)::value ? div_static(f[e], s, rcp) : f[e] / s;
-      u32x2 o;
-      if constexpr (INT8) {
-        uint32_t b[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float r = __builtin_rintf(f[e]);
-          sat += (fabsf(r) > 127.0f) ? 1u : 0u;
-          b[e] = int8_code(r);
-        }
-        o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-        o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+        for (int e = 0; e < 8; ++e) f[e] = F ? div_by_scale(f[e], s, rcp) : f[e] / s;
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          sat += (fabsf(f[e]) > 448.0f) ? 1u : 0u;
-          f[e] = clamp448(f[e]);
+          f[e] = F ? div_static(f[e], s, rcp) : f[e] / s;
+          if constexpr (INT8) {
+            f[e] = __builtin_rintf(f[e]);
+            sat += (fabsf(f[e]) > 127.0f) ? 1u : 0u;
+          } else {
+            sat += (fabsf(f[e]) > 448.0f) ? 1u : 0u;
+            f[e] = clamp448(f[e]);
+          }
         }
+      }
+      u32x2 o;
+      if constexpr (INT8) {
+        o.x = int8_code(f[0]) | (int8_code(f[1]) << 8) | (int8_code(f[2]) << 16) | (int8_code(f[3]) << 24);
+        o.y = int8_code(f[4]) | (int8_code(f[5]) << 8) | (int8_code(f[6]) << 16) | (int8_code(f[7]) << 24);
+      } else {
         o.x = pack_e4m3x4(f[0], f[1], f[2], f[3]);
         o.y = pack_e4m3x4(f[4], f[5], f[6], f[7]);
       }
-      __builtin_nontemporal_store(o, q + c);   // measured faster here than an ordinary store
+      if constexpr (NTS) __builtin_nontemporal_store(o, q + c);
+      else q[c] = o;
     }
   };
   if (shortcut) run(std::true_type{});
@@ -131,16 +152,27 @@ __global__ __launch_bounds__(256) void delayed_scale_kernel(float* __restrict__ 
   }
 }
 
-hipError_t launch_quantize_static(const void* x, int64_t M, int64_t K, int fmt, const float* scale,
-                                  void* q, uint32_t* saturated, float* amax, hipStream_t st) {
-  const int64_t nchunks = M * K / 8;
-  const int blocks = (int)((nchunks + 1023) / 1024);   // 4 chunks per thread, 256 threads
+template <int CH, bool NTL, bool NTS>
+static void launch_static(const void* x, int64_t nchunks, int fmt, const float* scale, void* q,
+                          uint32_t* saturated, float* amax, hipStream_t st) {
+  const int blocks = (int)((nchunks + 256 * CH - 1) / (256 * CH));
   if (fmt == 1)
-    hipLaunchKernelGGL(quant_static_kernel<true>, dim3(blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((quant_static_kernel<true, CH, NTL, NTS>), dim3(blocks), dim3(256), 0, st,
                        (const u32x4*)x, nchunks, scale, (u32x2*)q, saturated, amax);
   else
-    hipLaunchKernelGGL(quant_static_kernel<false>, dim3(blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((quant_static_kernel<false, CH, NTL, NTS>), dim3(blocks), dim3(256), 0, st,
                        (const u32x4*)x, nchunks, scale, (u32x2*)q, saturated, amax);
+}
+
+hipError_t launch_quantize_static(const void* x, int64_t M, int64_t K, int fmt, const float* scale,
+                                  void* q, uint32_t* saturated, float* amax, hipStream_t st) {
+  // Four chunks per thread up to 2^21 chunks (16 Mi elements), two above: measured on
+  // 2048 x 4096 (6.6 against 6.9 us) and on 2048 x 14336 to 16384 x 4096 (2-3% the other way).
+  const int64_t nchunks = M * K / 8;
+  if (nchunks <= ((int64_t)1 << 21))
+    launch_static<4, true, true>(x, nchunks, fmt, scale, q, saturated, amax, st);
+  else
+    launch_static<2, true, true>(x, nchunks, fmt, scale, q, saturated, amax, st);
   return hipGetLastError();
 }
 
