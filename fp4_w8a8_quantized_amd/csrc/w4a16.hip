@@ -23,8 +23,11 @@
 // lines); each lane keeps its K / 64 elements of X in registers for the whole kernel,
 // dequantizes its 32 codes per load with the biased conversion below and takes the products
 // with v_dot2 (two bf16 products accumulated in fp32 per instruction); the row's sum is reduced
-// across the wave with DPP moves. From two tokens on, the MFMA kernel above is faster (the
-// dot products grow with the tokens while the MFMA's are free up to 16).
+// across the wave with DPP moves. The vector unit's work is a large part of the time on wide
+// layers: the conversion at seven instructions per eight codes (one three-input bitwise op
+// per pair) instead of eleven took 14336 x 4096 from 8.6 to 7.8 us. From two tokens on, the
+// MFMA kernel above is faster (the dot products grow with the tokens while the MFMA's are
+// free up to 16).
 #include "common.h"
 #include "internal.h"
 
@@ -113,52 +116,55 @@ gemm_w4a16_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Groups of this wave: gi = wave + WPB * s for s < cnt. Weights (and scales) one group
-  // ahead, X loaded with the group; loads past the last group re-read it (in bounds, never
-  // accumulated).
+  // Groups of this wave: gi = wave + WPB * s for s < cnt. Weights, scales and X of the next
+  // group are loaded while this one is multiplied. (Two or four groups ahead measured slower:
+  // 6.5 and 7.0 against 5.9 us at 8 x 4096 x 4096.)
   const int cnt = (groups - wave + WPB - 1) / WPB;
-  auto gidx = [&](int s) { return wave + WPB * min(s, cnt - 1); };
   u32x4 wn[NW];
   float sn[NW][4];
-  auto load_w = [&](int s) {
-    const int gi = gidx(s);
+  u32x4 xn[MT][4];
+  auto load = [&](int s) {
+    const int gi = wave + WPB * s;
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       wn[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[j] + (int64_t)gi * kGB));
 #pragma unroll
       for (int r = 0; r < 4; ++r) sn[j][r] = (float)__builtin_bit_cast(_Float16, srow[j][r][gi]);
     }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xn[i][q] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)gi * kG + 8 * q);
   };
-  if (cnt > 0) load_w(0);
+  if (cnt > 0) load(0);
   for (int s = 0; s < cnt; ++s) {
-    const int gi = gidx(s);
     u32x4 wc[NW];
     float scur[NW][4];
+    u32x4 xv[MT][4];
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       wc[j] = wn[j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) scur[j][r] = sn[j][r];
     }
-    u32x4 xv[MT][4];
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        xv[i][p] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)gi * kG + 8 * p);
-    if (s + 1 < cnt) load_w(s + 1);
+      for (int q = 0; q < 4; ++q) xv[i][q] = xn[i][q];
+    if (s + 1 < cnt) load(s + 1);
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       const uint32_t ww[4] = {wc[j].x, wc[j].y, wc[j].z, wc[j].w};
       bf16x8 wf[4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) wf[p] = int4x8_to_bf16(ww[p]);
+      for (int q = 0; q < 4; ++q) wf[q] = int4x8_to_bf16(ww[q]);
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[p], __builtin_bit_cast(bf16x8, xv[i][p]), part, 0, 0, 0);
+        for (int q = 0; q < 4; ++q)
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[q], __builtin_bit_cast(bf16x8, xv[i][q]), part, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[r], scur[j][r], acc[j][i][r]);
       }
@@ -226,12 +232,32 @@ __device__ __forceinline__ void int4x8_to_bf16_biased(uint32_t w, uint32_t (&p)[
     p[i] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + i) << 16) | (uint32_t)i) | 0x43004300u;
 }
 
+// The same, paired differently: pair k (k < 4) is (136 + n_k, 136 + n_{k+4}), whose nibbles
+// sit 16 bits apart in the word. For a nibble c = n mod 16, c ^ 8 = n + 8, so the pair is
+// ((w >> 4k) & 0x000F000F) ^ 0x43084308: one three-input bitwise instruction (v_bitop3_b32)
+// and one shift for k > 0, seven instructions a word. The two masks are handed over in
+// registers (m, kc): as literals they would not fit one instruction. The partner operand pairs
+// x_k with x_{k+4}.
+__device__ __forceinline__ void int4x8_to_bf16_biased_k4(uint32_t w, uint32_t m, uint32_t kc,
+                                                         uint32_t (&p)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) p[k] = ((w >> (4 * k)) & m) ^ kc;
+}
+
+// A constant in a vector register that the compiler cannot fold back into an instruction.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
+}
+
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kGvChunk = 2048;          // K elements per load of a whole wave (one kilobyte of codes)
 
 // Wave w of the grid takes weight rows w, w + W, ... (W waves in all), one row in flight: L
-// loads of 16 bytes per lane (chunk 64 t + l of the row, K offsets 32 (64 t + l) .. +31).
+// loads of 16 bytes per lane (chunk 64 t + l of the row, K offsets 32 (64 t + l) .. +31). (Two
+// rows in flight measured slower: 4.8 against 4.5 us at 4096 rows, 8.7 against 8.5 at 14336.)
 template <int L>
 __global__ void __launch_bounds__(256)
 gemm_w4a16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq,
@@ -266,14 +292,20 @@ gemm_w4a16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
     const u32x4* xp = xl + 4 * (64 * t + lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
+      // Eight bf16 of X, (x0 x1) (x2 x3) (x4 x5) (x6 x7) as words, to the conversion's
+      // pairs (x0 x4) (x1 x5) (x2 x6) (x3 x7).
       const u32x4 v = xp[q];
-      xw[t][4 * q] = v.x; xw[t][4 * q + 1] = v.y; xw[t][4 * q + 2] = v.z; xw[t][4 * q + 3] = v.w;
+      xw[t][4 * q] = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+      xw[t][4 * q + 1] = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+      xw[t][4 * q + 2] = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+      xw[t][4 * q + 3] = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
     }
     float sum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sum += __uint_as_float(xw[t][e] << 16) + __uint_as_float(xw[t][e] & 0xFFFF0000u);
     xb[t] = 136.0f * sum;
   }
+  const uint32_t m4 = vreg_const(0x000F000Fu), kc4 = vreg_const(0x43084308u);
   for (int i = 0; i < cnt; ++i) {
     float acc = 0.f;
 #pragma unroll
@@ -282,11 +314,11 @@ gemm_w4a16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
       float d = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        uint32_t p[4];
-        int4x8_to_bf16_biased(w4[j], p);
+        uint32_t pk[4];
+        int4x8_to_bf16_biased_k4(w4[j], m4, kc4, pk);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p[e]),
+          d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[e]),
                                               __builtin_bit_cast(bf16x2, xw[t][4 * j + e]), d, false);
       }
       acc = __builtin_fmaf(d - xb[t], (float)__builtin_bit_cast(_Float16, sb[t]), acc);
@@ -300,7 +332,8 @@ gemm_w4a16_gemv_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict
 template <int L>
 hipError_t launch_w4a16_gemv(const void* x, const void* wq, const uint16_t* sc, int64_t N, int64_t K,
                              void* y, hipStream_t st) {
-  // About two rows per wave, at most 1024 workgroups (measured at 4096 and 14336 rows).
+  // About two rows per wave, at most 1024 workgroups (measured at 4096 and 14336 rows; one
+  // row per wave, or 4096 workgroups, measured slower).
   const int64_t want = (N + 7) / 8;
   const int blocks = (int)(want < 1 ? 1 : (want > 1024 ? 1024 : want));
   hipLaunchKernelGGL((gemm_w4a16_gemv_kernel<L>), dim3((unsigned)blocks), dim3(256), 0, st,

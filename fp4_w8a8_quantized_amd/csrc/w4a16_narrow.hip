@@ -72,7 +72,7 @@ __device__ __forceinline__ bf16x8 w4n_codes_to_bf16_biased(uint32_t w) {
   return __builtin_bit_cast(bf16x8, p);
 }
 
-template <int BM, int BN, int WK, int ST>
+template <int BM, int BN, int WK, int ST, int XR>
 __global__ void __launch_bounds__(256)
 gemm_w4a16_narrow_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ wq,
                          const uint8_t* __restrict__ sc, int M, int N, int K, int groups, int kblocks,
@@ -82,11 +82,14 @@ gemm_w4a16_narrow_kernel(const uint8_t* __restrict__ x, const uint8_t* __restric
   constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   constexpr int SM = TM / 16, SN = TN / 16;          // 16 x 16 subtiles per wave
   static_assert(WK * WMN == 4 && SM >= 1 && SN >= 1 && SM * 16 * WM == BM && SN * 16 * WN == BN, "tile shape");
+  // XR token rows of X are staged per tile: BM, or 8 of a 16-row tile when M <= 8, whose
+  // fragment rows 8-15 then read rows 0-7 again (their outputs are never stored).
+  static_assert(XR == BM || (XR == 8 && BM == 16), "staged X rows");
   static_assert(kW4nGroups % WK == 0, "every wave takes the same number of groups per stage");
   constexpr int SROWS = BN < 32 ? 32 : BN;           // scale rows per stage (32 per 4-byte load)
-  constexpr int XST = BM * kW4nXRow, WST = BN * kW4nWRow, SST = SROWS * kW4nSRow;
+  constexpr int XST = XR * kW4nXRow, WST = BN * kW4nWRow, SST = SROWS * kW4nSRow;
   constexpr int STAGE = XST + WST + SST;
-  constexpr int NDX = BM, NDW = BN / 4, NDS = SROWS / 32;
+  constexpr int NDX = XR, NDW = BN / 4, NDS = SROWS / 32;
   constexpr int ND = NDX + NDW + NDS;                // loads per stage
   constexpr int NQ = (ND + 3) / 4;                   // loads per wave per stage, at most
   constexpr int NDR = ND % 4;                        // waves below NDR issue NQ, others NQ - 1
@@ -180,7 +183,7 @@ gemm_w4a16_narrow_kernel(const uint8_t* __restrict__ x, const uint8_t* __restric
       bf16x8 xf[SM][4];
 #pragma unroll
       for (int i = 0; i < SM; ++i) {
-        const int row = wm * TM + 16 * i + fr;
+        const int row = (wm * TM + 16 * i + fr) % XR;
 #pragma unroll
         for (int p = 0; p < 4; ++p)
           xf[i][p] = *reinterpret_cast<const bf16x8*>(X + row * kW4nXRow + (((16 * q + 4 * g + p) ^ (row & 15)) << 4));
@@ -258,12 +261,13 @@ gemm_w4a16_narrow_kernel(const uint8_t* __restrict__ x, const uint8_t* __restric
   }
 }
 
-template <int BM, int BN, int WK, int ST>
+template <int BM, int BN, int WK, int ST, int XR = BM>
 hipError_t launch_w4n(const void* x, const void* wq, const uint16_t* sc, int64_t M, int64_t N, int64_t K,
                       void* y, hipStream_t st) {
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles = tiles_m * (int)((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_w4a16_narrow_kernel<BM, BN, WK, ST>), dim3((unsigned)tiles), dim3(256), 0, st,
+  if (XR < BM && M > XR) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_w4a16_narrow_kernel<BM, BN, WK, ST, XR>), dim3((unsigned)tiles), dim3(256), 0, st,
                      (const uint8_t*)x, (const uint8_t*)wq, (const uint8_t*)sc, (int)M, (int)N, (int)K,
                      (int)(K / 128), (int)(K / 512), tiles_m, (uint16_t*)y);
   return hipGetLastError();
@@ -277,7 +281,8 @@ int64_t w4n_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // graph replay, against the kernels used before: the decode kernel whose waves split K, and
 // the LDS-staged kernel above 16-32 tokens):
 //   9-16 tokens on 8193-16384 outputs: 16 x 32 (8 x 14336 14.0 -> 12.5 us, 16 x 14336
-//     16.0 -> 12.8);
+//     16.0 -> 12.8); up to 8 tokens the same tile stages only 8 rows of X (8 x 14336 12.0 ->
+//     11.5 us, 4 x 14336 11.8 -> 11.5);
 //   17-32 tokens: 16 x 16 up to 4096 outputs (32 x 4096 11.0 -> 8.8 us), 16 x 32 up to
 //     8192 (24 x 6144 16.8 -> 12.1), 32 x 64 up to 16384 (32 x 14336 25.6 -> 19.6);
 //   33-64 tokens: 16 x 32 where one round of them (two per CU) covers the output (64 x 4096
@@ -289,6 +294,7 @@ int64_t w4n_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // 7.2 us): its 8 waves per workgroup hide the load latency that this kernel's stages expose.
 int w4a16_narrow_config(int64_t M, int64_t N, int64_t K) {
   if (M < 2 || M > 128 || N < 1 || K % 512 != 0) return -1;
+  if (M <= 8) return (N > 8192 && w4n_cdiv(N, 32) <= 512) ? 4 : -1;
   if (M <= 16) return (N > 8192 && w4n_cdiv(N, 32) <= 512) ? 1 : -1;
   if (M <= 32) {
     if (2 * w4n_cdiv(N, 16) <= 512) return 0;
@@ -307,6 +313,7 @@ hipError_t launch_gemm_w4a16_narrow(const void* x, const void* wq, const uint16_
     case 0: return launch_w4n<16, 16, 4, 3>(x, wq, sc, M, N, K, y, st);
     case 1: return launch_w4n<16, 32, 2, 3>(x, wq, sc, M, N, K, y, st);
     case 2: return launch_w4n<32, 64, 1, 3>(x, wq, sc, M, N, K, y, st);
+    case 4: return launch_w4n<16, 32, 2, 3, 8>(x, wq, sc, M, N, K, y, st);
     default: return hipErrorInvalidValue;
   }
 }
