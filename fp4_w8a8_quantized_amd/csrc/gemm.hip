@@ -13,8 +13,8 @@
 //    the output: narrow tiles sized to the token count (gemm_narrow.hip);
 //  - one token that the vector kernel does not take: the weight-streaming split-K kernel
 //    (gemm_skinny.hip);
-//  - otherwise the prefill kernels: FP8 on 16x16x128 MFMAs (gemm_pp.hip), INT8
-//    on 32x32x32 MFMAs (gemm_mx_pp.hip, which it shares with MXFP4).
+//  - otherwise the prefill kernels (gemm_pp.hip, and gemm_solo.hip for 128-wide tiles): FP8
+//    on 16x16x128 MFMAs, INT8 on pairs of 16x16x64 MFMAs over the same fragments.
 #include "common.h"
 #include "internal.h"
 
@@ -26,8 +26,7 @@ hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const fl
   if (use_gemm_gemv(M, N, K)) return launch_gemm_gemv(xq, sx, wq, sw, N, K, fmt, y, st, ep);
   if (use_gemm_narrow(M, N, K)) return launch_gemm_narrow(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
   if (M == 1) return launch_gemm_skinny(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
-  if (fmt == 0) return launch_gemm_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
-  return launch_gemm_int8_pp(xq, sx, wq, sw, M, N, K, y, st, ep);
+  return launch_gemm_pp(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
 }
 
 }  // namespace w8a8

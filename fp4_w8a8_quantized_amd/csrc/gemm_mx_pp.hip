@@ -1,15 +1,11 @@
-// MXFP4 x MXFP4 and INT8 x INT8 GEMMs on gfx950 with two waves per SIMD taking turns
-// ("ping-pong"), both on 32 x 32 MFMAs whose operands are 16 bytes per lane:
-//   MXFP4  y = bf16( sum_b 2^(ex[m,b]-127) 2^(ew[n,b]-127) sum_{k in b} dec4(xq) dec4(wq) )
-//          for OCP MXFP4 operands (E2M1 elements, one E8M0 scale per 32 along K; "Low-bit
-//          LLM Weights and Activations" §2.4). The E8M0 scales go straight into the scale
-//          operands of v_mfma_scale_f32_32x32x64_f8f6f4, so scaling costs no vector work.
-//   INT8   y = epilogue( fp32(fp32(acc_i32) s_x[m]) s_w[n] ),  acc_i32 = sum_k xq wq
-//          (v_mfma_i32_32x32x32_i8; SmoothQuant W8A8, "Low-bit LLM Weights and
-//          Activations" §4 and "FP8 and INT8 Inference" §5: each product rounded on its
-//          own, in that order, so that outputs are exact functions of the codes), with the
-//          epilogue's bias, activation and bf16 or FP8 output ("FP8 and INT8 Inference"
-//          §6-9).
+// MXFP4 x MXFP4 GEMM on gfx950 with two waves per SIMD taking turns ("ping-pong"), on
+// 32 x 32 MFMAs whose operands are 16 bytes per lane:
+//   y = bf16( sum_b 2^(ex[m,b]-127) 2^(ew[n,b]-127) sum_{k in b} dec4(xq) dec4(wq) )
+// for OCP MXFP4 operands (E2M1 elements, one E8M0 scale per 32 along K; "Low-bit LLM
+// Weights and Activations" §2.4). The E8M0 scales go straight into the scale operands of
+// v_mfma_scale_f32_32x32x64_f8f6f4, so scaling costs no vector work. It takes the shapes
+// whose 256 x 256 tiles would not fill a round of the CUs (the one-wave-per-SIMD kernel,
+// gemm_mx_solo.hip, takes the rest).
 //
 // Schedule: as the FP8 ping-pong kernel. A 512-thread workgroup computes a 256 x 128 tile;
 // waves 0-3 (group A) and 4-7 (group B) alternate an LDS phase (fragments and scales of a
@@ -20,10 +16,8 @@
 // E8M0 scales of each step into a small LDS area of the stage one step ahead.
 //
 // Fragments: lane l reads row l & 31 and the 16-byte chunks h, h+2, h+4, h+6 (h = l >> 5);
-// chunk 2q + h is the lane's 16 bytes for the q-th MFMA of the step: for MXFP4 the
-// 32-element block 2q + h, whose scale byte the lane supplies; for INT8 16 of the 32
-// elements of K that MFMA q covers (the other lane half holds the rest). INT8 has no
-// scales in the K loop: group A only waits at the barriers.
+// chunk 2q + h is the lane's 16 bytes for the q-th MFMA of the step: the 32-element block
+// 2q + h, whose scale byte the lane supplies.
 #include "common.h"
 #include "internal.h"
 
@@ -52,20 +46,14 @@ __device__ __forceinline__ void mx_barrier() { asm volatile("s_barrier" ::: "mem
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-template <bool I8, bool OF8, int BN>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
-                  const uint8_t* __restrict__ wq, const void* __restrict__ swp, int M, int N,
-                  int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store,
-                  Epilogue ep) {
-  static_assert(I8 || (!OF8 && BN == kMxBN), "the MXFP4 GEMM writes bf16 from 128-wide tiles");
-  constexpr int BM = kMxBM;
+gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ sx,
+                  const uint8_t* __restrict__ wq, const uint8_t* __restrict__ sw, int M, int N,
+                  int Kb, int ksteps, uint16_t* __restrict__ y, int tiles_m, int vec_store) {
+  constexpr int BM = kMxBM, BN = kMxBN;
   constexpr int SM = 2, SN = BN / 64;               // 32 x 32 subtiles per wave (64 x BN/2)
   constexpr int XT = BM * 128, WT = BN * 128;       // code bytes of a stage
-  constexpr int SCX = I8 ? 0 : BM * 8, SCW = I8 ? 0 : BN * 8;   // MXFP4 scale bytes of a stage
-  const uint8_t* __restrict__ sx = reinterpret_cast<const uint8_t*>(sxp);
-  const uint8_t* __restrict__ sw = reinterpret_cast<const uint8_t*>(swp);
-  uint16_t* __restrict__ y = reinterpret_cast<uint16_t*>(yp);
+  constexpr int SCX = BM * 8, SCW = BN * 8;         // scale bytes of a stage
   constexpr int STAGE = XT + WT + SCX + SCW;
   constexpr int XI = BM / 32, WI = BN / 32;         // 1 KB loads per group-B wave per step
   constexpr int DMA = XI + WI, DC = DMA / 2;        // of which issued during the MFMA phase
@@ -124,12 +112,11 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
 #pragma unroll
   for (int q = 0; q < 4; ++q) fo[q] = mx_off(fr, 2 * q + h);
 
-  typedef typename std::conditional<I8, i32x16, f32x16>::type acc_t;
-  acc_t acc[SN][SM];
+  f32x16 acc[SN][SM];
 #pragma unroll
   for (int j = 0; j < SN; ++j)
 #pragma unroll
-    for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{};
+    for (int i = 0; i < SM; ++i) acc[j][i] = f32x16{};
   i32x4 xf[SM][4], wf[SN][4];
   int ex[SM][4], ew[SN][4];                          // scale byte per subtile and MFMA
 
@@ -145,10 +132,6 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     for (int j = 0; j < SN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) wf[j][q] = *reinterpret_cast<const i32x4*>(W + (wrow0 + 32 * j) * 128 + fo[q]);
-    if constexpr (I8) {
-      __builtin_amdgcn_s_waitcnt(mx_wait(63, 0));  // this wave's reads of the stage done
-      return;
-    }
     u32x2 sxv[SM], swv[SN];
 #pragma unroll
     for (int i = 0; i < SM; ++i) sxv[i] = *reinterpret_cast<const u32x2*>(SC + (xrow0 + 32 * i + fr) * 8);
@@ -168,13 +151,9 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   // MFMA number u = (i * SN + j) * 4 + q. FP4 operands occupy the low 16 bytes.
   auto mfma_one = [&](int u) {
     const int q = u & 3, j = (u >> 2) % SN, i = (u >> 2) / SN;
-    if constexpr (I8) {
-      acc[j][i] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[j][q], xf[i][q], acc[j][i], 0, 0, 0);
-    } else {
-      const i32x8_t a = {wf[j][q][0], wf[j][q][1], wf[j][q][2], wf[j][q][3], 0, 0, 0, 0};
-      const i32x8_t bb = {xf[i][q][0], xf[i][q][1], xf[i][q][2], xf[i][q][3], 0, 0, 0, 0};
-      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[j][i], 4, 4, 0, ew[j][q], 0, ex[i][q]);
-    }
+    const i32x8_t a = {wf[j][q][0], wf[j][q][1], wf[j][q][2], wf[j][q][3], 0, 0, 0, 0};
+    const i32x8_t bb = {xf[i][q][0], xf[i][q][1], xf[i][q][2], xf[i][q][3], 0, 0, 0, 0};
+    acc[j][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bb, acc[j][i], 4, 4, 0, ew[j][q], 0, ex[i][q]);
   };
   auto mfma_range = [&](int lo, int hi) {
 #pragma unroll
@@ -192,38 +171,15 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
     }
   };
 
-  // INT8: the epilogue's scales are loaded up front (before any direct-to-LDS load, so
-  // group B's hand-counted waits see only its loads); their latency hides behind the loop.
-  // The 192-wide tile cannot spare the column scales' registers during the loop and loads
-  // them after it. Lane l holds output row 32 i + (l & 31) and columns
-  // 32 j + 8 q + 4 (l >> 5) + r.
-  constexpr bool LATE_SN = (BN > 128);
-  float esm[SM], esn[SN][4][4];
-  auto load_esn = [&]() {
-    const float* swf = reinterpret_cast<const float*>(swp);
-#pragma unroll
-    for (int j = 0; j < SN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) esn[j][q][r] = swf[min(n0 + wrow0 + 32 * j + 8 * q + 4 * h + r, N - 1)];
-  };
-  if constexpr (I8) {
-    const float* sxf = reinterpret_cast<const float*>(sxp);
-#pragma unroll
-    for (int i = 0; i < SM; ++i) esm[i] = sxf[min(m0 + xrow0 + 32 * i + fr, M - 1)];
-    if constexpr (!LATE_SN) load_esn();
-  }
-
   // Prologue: B loads the codes of steps 0 and 1; A stores step 0's scales and holds step
-  // 1's (MXFP4); step 0 is published by the barrier.
+  // 1's; step 0 is published by the barrier.
   if (grp == 1) {
 #pragma unroll
     for (int d = 0; d < DMA; ++d) dma_one(0, 0, d);
 #pragma unroll
     for (int d = 0; d < DMA; ++d) dma_one(min(1, ksteps - 1), 1, d);
     __builtin_amdgcn_s_waitcnt(mx_wait(DMA, 15));
-  } else if constexpr (!I8) {
+  } else {
     load_sc(0);
     store_sc(0);
     if (ksteps > 1) load_sc(1);
@@ -233,7 +189,7 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   // Both groups pass 3 * ksteps + 1 barriers in the loop part.
   if (grp == 0) {
     for (int ks = 0; ks < ksteps; ++ks) {
-      if (!I8 && ks + 1 < ksteps) {                  // scales one step ahead
+      if (ks + 1 < ksteps) {                         // scales one step ahead
         store_sc((ks + 1) & 1);
         if (ks + 2 < ksteps) load_sc(ks + 2);
       }
@@ -275,80 +231,9 @@ gemm_mx_pp_kernel(const uint8_t* __restrict__ xq, const void* __restrict__ sxp,
   }
 
   // ---- epilogue
-  if constexpr (I8 && LATE_SN) load_esn();
   __builtin_amdgcn_s_waitcnt(mx_wait(0, 0));
   mx_barrier();
-  if constexpr (I8) {
-    // Dequantize (two separately rounded products, in the pages' order), add the bias,
-    // activate, convert (bf16, or E4M3FN of clamp(v / s_out) with an IEEE division), stage
-    // the tile through LDS and write whole 16-byte row chunks.
-    constexpr int ES = OF8 ? 1 : 2;                  // output bytes per element
-    constexpr int RS = BN * ES + 16;                 // padded rows
-    static_assert(BM * RS <= 2 * STAGE, "output tile must fit in the pipeline LDS");
-    const bool has_bias = ep.bias != nullptr;
-    epi_dispatch(ep.act, has_bias, [&](auto act_c, auto bias_c) {
-      constexpr int ACT = decltype(act_c)::value;
-      constexpr bool BIAS = decltype(bias_c)::value;
-#pragma unroll
-      for (int i = 0; i < SM; ++i) {
-        const int rl = xrow0 + 32 * i + fr;
-#pragma unroll
-        for (int j = 0; j < SN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int cl = wrow0 + 32 * j + 8 * q + 4 * h;
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              v[r] = mul_rn(mul_rn((float)acc[j][i][4 * q + r], esm[i]), esn[j][q][r]);
-              if constexpr (BIAS) v[r] = add_rn(v[r], bf16_lo(ep.bias[min(n0 + cl + r, N - 1)]));
-              v[r] = epi_act<ACT>(v[r]);
-            }
-            if constexpr (OF8) {
-              *reinterpret_cast<uint32_t*>(lds + rl * RS + cl) =
-                  pack_e4m3x4(epi_requant<true>(v[0], ep.s_out, ep.inv_s_out), epi_requant<true>(v[1], ep.s_out, ep.inv_s_out),
-                              epi_requant<true>(v[2], ep.s_out, ep.inv_s_out), epi_requant<true>(v[3], ep.s_out, ep.inv_s_out));
-            } else {
-              const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-              *reinterpret_cast<u32x2*>(lds + rl * RS + cl * 2) = o;
-            }
-          }
-      }
-    });
-    __builtin_amdgcn_s_waitcnt(mx_wait(63, 0));
-    mx_barrier();
-    constexpr int EPC = 16 / ES;                     // output elements per 16-byte chunk
-    constexpr int CPR = BN / EPC;                    // chunks per output row
-    constexpr int ITERS = BM * CPR / kMxThreads;
-    static_assert(ITERS * kMxThreads == BM * CPR, "whole chunks per thread");
-    u32x4 ov[ITERS];
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int c = t + it * kMxThreads;
-      const int rl = c / CPR, ch = c - rl * CPR;
-      ov[it] = *reinterpret_cast<const u32x4*>(lds + rl * RS + ch * 16);
-    }
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int c = t + it * kMxThreads;
-      const int rl = c / CPR, ch = c - rl * CPR;
-      const int m = m0 + rl, n = n0 + ch * EPC;
-      if (m >= M || n >= N) continue;
-      uint8_t* yr = reinterpret_cast<uint8_t*>(yp) + ((size_t)m * N + n) * ES;
-      if (vec_store && n + EPC - 1 < N) {
-        *reinterpret_cast<u32x4*>(yr) = ov[it];
-      } else {
-        const uint32_t w4[4] = {ov[it].x, ov[it].y, ov[it].z, ov[it].w};
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          if (n + e >= N) break;
-          if constexpr (OF8) yr[e] = (uint8_t)((w4[e >> 2] >> (8 * (e & 3))) & 0xFFu);
-          else reinterpret_cast<uint16_t*>(yr)[e] = (uint16_t)((w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        }
-      }
-    }
-    return;
-  } else {
+  {
     constexpr int RS = BN * 2 + 16;                    // padded rows
     static_assert(BM * RS <= 2 * STAGE, "output tile must fit in the pipeline LDS");
     // In the 32x32 result (A = W fragment, B = X fragment), lane l holds output row
@@ -409,40 +294,10 @@ hipError_t launch_gemm_mxfp4(const void* xq, const uint8_t* sx, const void* wq, 
     return launch_gemm_mx_solo(xq, sx, wq, sw, M, N, K, y, st);
   const int tiles_m = (int)((M + kMxBM - 1) / kMxBM);
   const int tiles_n = (int)((N + kMxBN - 1) / kMxBN);
-  hipLaunchKernelGGL((gemm_mx_pp_kernel<false, false, kMxBN>), dim3((unsigned)(tiles_m * tiles_n)),
-                     dim3(kMxThreads), 0, st, (const uint8_t*)xq, (const void*)sx,
-                     (const uint8_t*)wq, (const void*)sw, (int)M, (int)N, (int)(K / 2),
-                     (int)(K / 256), y, tiles_m, (int)((N % 8) == 0), Epilogue{});
+  hipLaunchKernelGGL(gemm_mx_pp_kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMxThreads), 0, st,
+                     (const uint8_t*)xq, sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)(K / 2),
+                     (int)(K / 256), (uint16_t*)y, tiles_m, (int)((N % 8) == 0));
   return hipGetLastError();
-}
-
-template <int BN>
-hipError_t launch_i8(const void* xq, const float* sx, const void* wq, const float* sw, int64_t M,
-                     int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
-  const int tiles_m = (int)((M + kMxBM - 1) / kMxBM);
-  const int tiles_n = (int)((N + BN - 1) / BN);
-  const dim3 grid((unsigned)(tiles_m * tiles_n)), block(kMxThreads);
-  if (ep.out_fp8)
-    hipLaunchKernelGGL((gemm_mx_pp_kernel<true, true, BN>), grid, block, 0, st, (const uint8_t*)xq,
-                       (const void*)sx, (const uint8_t*)wq, (const void*)sw, (int)M, (int)N,
-                       (int)K, (int)(K / 128), y, tiles_m, (int)((N % 16) == 0), ep);
-  else
-    hipLaunchKernelGGL((gemm_mx_pp_kernel<true, false, BN>), grid, block, 0, st, (const uint8_t*)xq,
-                       (const void*)sx, (const uint8_t*)wq, (const void*)sw, (int)M, (int)N,
-                       (int)K, (int)(K / 128), y, tiles_m, (int)((N % 8) == 0), ep);
-  return hipGetLastError();
-}
-
-// INT8 tile width: as for FP8, the width whose waves of workgroups over the 256 CUs cost
-// least, each weighted by its steady-state efficiency (192-wide tiles read fewer bytes per
-// MFMA: 64 x 96 wave tiles, 24 MFMAs on 20 fragment reads per step).
-hipError_t launch_gemm_int8_pp(const void* xq, const float* sx, const void* wq, const float* sw,
-                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
-                               const Epilogue& ep) {
-  const int64_t tm = (M + kMxBM - 1) / kMxBM;
-  auto cost = [&](int64_t bn, int64_t per_tile) { return ((tm * ((N + bn - 1) / bn) + 255) / 256) * per_tile; };
-  if (cost(192, 240) < cost(128, 194)) return launch_i8<192>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  return launch_i8<128>(xq, sx, wq, sw, M, N, K, y, st, ep);
 }
 
 }  // namespace w8a8

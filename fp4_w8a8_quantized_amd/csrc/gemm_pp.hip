@@ -1,5 +1,9 @@
-// FP8 W8A8 GEMM on gfx950 with two waves per SIMD taking turns ("ping-pong"):
-//   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )     (v_mfma 16x16x128 f8f6f4)
+// W8A8 GEMM on gfx950 with two waves per SIMD taking turns ("ping-pong"):
+//   FP8   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )   (v_mfma 16x16x128 f8f6f4)
+//   INT8  y = epilogue( fp32(fp32(acc_i32) s_x[m]) s_w[n] ),  acc_i32 = sum_k xq wq
+//         (two v_mfma_i32_16x16x64_i8 per subtile and step on the same 32-byte fragments;
+//         SmoothQuant W8A8, each product of the dequantization rounded on its own, in that
+//         order, so that outputs are exact functions of the codes)
 // with the scale factoring of "FP8 and FP4 inference, SmoothQuant and activation
 // quantization" (Scale granularity) and the epilogue of "FP8 and INT8 Inference" §6-9.
 //
@@ -45,6 +49,8 @@
 // and the tile's s_w two steps ahead and publishes their products to a double-buffered
 // 1 KB LDS area, laid out so that each lane reads its four rows with one 16-byte read.
 // Tiles are 128 wide, one weight block, so every column of a tile shares s_w.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -73,13 +79,14 @@ constexpr int pp_wait(int vm, int lgkm) {
 
 __device__ __forceinline__ void pp_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int BN, bool OF8, bool BLK>
+template <int KIND, int BN, bool OF8, bool BLK>
 __global__ void __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
                int Kb, int ksteps, void* __restrict__ yp, int tiles_m, int vec_store, Epilogue ep) {
   constexpr int BM = kPPBM;
-  static_assert(!BLK || (BN == 128 && !OF8), "block scales: 128-wide tiles (one weight block), bf16 out");
+  static_assert(!BLK || (BN == 128 && !OF8 && KIND == 0), "block scales: FP8, 128-wide tiles (one weight block), bf16 out");
+  typedef typename std::conditional<KIND == 1, i32x4, f32x4>::type acc_t;
   // Wave tiles: 128 x 48 at BN = 192 (2 x 4 waves); 64 x BN/2 otherwise (4 x 2 waves): at
   // BN = 128 that reads 8 fragments per step instead of 10 for the same 64 accumulators, and
   // at BN = 224 (64 x 112) 11 fragments for 28 MFMAs.
@@ -144,11 +151,11 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     return frag_t{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
   };
 
-  f32x4 acc[SN][SM];
+  acc_t acc[SN][SM];
 #pragma unroll
   for (int j = 0; j < SN; ++j)
 #pragma unroll
-    for (int i = 0; i < SM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{};
   frag_t xf[SM], wf[SN];
 
   constexpr int T = SM * SN;
@@ -198,6 +205,12 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     if constexpr (BLK) {
       if (tt >= PD) promote(tt - PD);
       pp[tt % PD] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+    } else if constexpr (KIND == 1) {
+      // INT8: the fragment's two 16-byte chunks are the two 64-deep halves of the step.
+      acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{wf[j][0], wf[j][1], wf[j][2], wf[j][3]},
+                                                       i32x4{xf[i][0], xf[i][1], xf[i][2], xf[i][3]}, acc[j][i], 0, 0, 0);
+      acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{wf[j][4], wf[j][5], wf[j][6], wf[j][7]},
+                                                       i32x4{xf[i][4], xf[i][5], xf[i][6], xf[i][7]}, acc[j][i], 0, 0, 0);
     } else {
       acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], xf[i], acc[j][i], 0, 0, 0, 0, 0, 0);
     }
@@ -345,14 +358,15 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = BLK ? acc[j][i][r] : acc[j][i][r] * (esm[i] * esn[j][r]);
+          if constexpr (KIND == 1) v[r] = mul_rn(mul_rn((float)acc[j][i][r], esm[i]), esn[j][r]);
+          else v[r] = BLK ? acc[j][i][r] : acc[j][i][r] * (esm[i] * esn[j][r]);
           if constexpr (BIAS) v[r] = add_rn(v[r], bf16_lo(ep.bias[min(n0 + cl + r, N - 1)]));
           v[r] = epi_act<ACT>(v[r]);
         }
         if constexpr (OF8) {
           *reinterpret_cast<uint32_t*>(lds + opos(rl, cl)) =
-              pack_e4m3x4(epi_requant<false>(v[0], ep.s_out, ep.inv_s_out), epi_requant<false>(v[1], ep.s_out, ep.inv_s_out),
-                          epi_requant<false>(v[2], ep.s_out, ep.inv_s_out), epi_requant<false>(v[3], ep.s_out, ep.inv_s_out));
+              pack_e4m3x4(epi_requant<KIND == 1>(v[0], ep.s_out, ep.inv_s_out), epi_requant<KIND == 1>(v[1], ep.s_out, ep.inv_s_out),
+                          epi_requant<KIND == 1>(v[2], ep.s_out, ep.inv_s_out), epi_requant<KIND == 1>(v[3], ep.s_out, ep.inv_s_out));
         } else {
           const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2*>(lds + opos(rl, cl * 2)) = o;
@@ -396,13 +410,13 @@ gemm_pp_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
   }
 }
 
-template <int BN, bool OF8, bool BLK = false>
+template <int KIND, int BN, bool OF8, bool BLK = false>
 hipError_t launch_pp(const void* xq, const float* sx, const void* wq, const float* sw, int64_t M,
                      int64_t N, int64_t K, void* y, hipStream_t st, const Epilogue& ep) {
   const int tiles_m = (int)((M + kPPBM - 1) / kPPBM);
   const int tiles_n = (int)((N + BN - 1) / BN);
   const int vec = OF8 ? (N % 16) == 0 : (N % 8) == 0;
-  hipLaunchKernelGGL((gemm_pp_kernel<BN, OF8, BLK>), dim3((unsigned)(tiles_m * tiles_n)),
+  hipLaunchKernelGGL((gemm_pp_kernel<KIND, BN, OF8, BLK>), dim3((unsigned)(tiles_m * tiles_n)),
                      dim3(kPPThreads), 0, st, (const uint8_t*)xq, sx, (const uint8_t*)wq, sw,
                      (int)M, (int)N, (int)K, (int)(K / 128), y, tiles_m, vec, ep);
   return hipGetLastError();
@@ -416,7 +430,7 @@ hipError_t launch_pp(const void* xq, const float* sx, const void* wq, const floa
 // reads and barriers). 224 wins where it removes a partial wave, as for 2048 x 28672
 // (1024 tiles, four full waves, against 1200 tiles of 192).
 hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const float* sw,
-                          int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                          int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                           const Epilogue& ep) {
   const int64_t tm = (M + kPPBM - 1) / kPPBM;
   auto cost = [&](int64_t bn, int64_t per_tile) { return ((tm * ((N + bn - 1) / bn) + 255) / 256) * per_tile; };
@@ -427,22 +441,26 @@ hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const
   // 2048 x 4096 x 14336: 102.5 -> 93.4 us; 4096 x 4096 x 4096: 64.7 -> 62.1 us). At four
   // rounds (8192 x 4096 x 14336) it measured 3% slower.
   if (bn == 128 && tm * ((N + 127) / 128) <= 512)
-    return launch_gemm_solo(xq, sx, wq, sw, M, N, K, y, st, ep);
-  if (ep.out_fp8) {
-    if (bn == 224) return launch_pp<224, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
-    return bn == 192 ? launch_pp<192, true>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                     : launch_pp<128, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  }
-  if (bn == 224) return launch_pp<224, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
-  return bn == 192 ? launch_pp<192, false>(xq, sx, wq, sw, M, N, K, y, st, ep)
-                   : launch_pp<128, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    return launch_gemm_solo(xq, sx, wq, sw, M, N, K, fmt, y, st, ep);
+  auto go = [&](auto kind_c) {
+    constexpr int KD = decltype(kind_c)::value;
+    if (ep.out_fp8) {
+      if (bn == 224) return launch_pp<KD, 224, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
+      return bn == 192 ? launch_pp<KD, 192, true>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                       : launch_pp<KD, 128, true>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    }
+    if (bn == 224) return launch_pp<KD, 224, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    return bn == 192 ? launch_pp<KD, 192, false>(xq, sx, wq, sw, M, N, K, y, st, ep)
+                     : launch_pp<KD, 128, false>(xq, sx, wq, sw, M, N, K, y, st, ep);
+  };
+  return fmt == 1 ? go(std::integral_constant<int, 1>{}) : go(std::integral_constant<int, 0>{});
 }
 
 // Block-scaled FP8 (s_x [M, K/128], s_w [ceil(N/128), K/128]): 256 x 128 tiles, bf16 out.
 hipError_t launch_gemm_blockscaled(const void* xq, const float* sx, const void* wq,
                                    const float* sw, int64_t M, int64_t N, int64_t K, void* y,
                                    hipStream_t st) {
-  return launch_pp<128, false, true>(xq, sx, wq, sw, M, N, K, y, st, Epilogue{});
+  return launch_pp<0, 128, false, true>(xq, sx, wq, sw, M, N, K, y, st, Epilogue{});
 }
 
 }  // namespace w8a8

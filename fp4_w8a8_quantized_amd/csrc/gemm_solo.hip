@@ -1,5 +1,7 @@
-// FP8 W8A8 GEMM on gfx950 with one wave per SIMD:
-//   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )     (v_mfma 16x16x128 f8f6f4)
+// W8A8 GEMM on gfx950 with one wave per SIMD:
+//   FP8   y = epilogue( s_x[m] s_w[n] sum_k dec(xq[m,k]) dec(wq[n,k]) )   (v_mfma 16x16x128 f8f6f4)
+//   INT8  y = epilogue( fp32(fp32(acc_i32) s_x[m]) s_w[n] )   (two v_mfma_i32_16x16x64_i8 per
+//         subtile and step on the same fragments; the INT8 form of the ping-pong kernel)
 // with the scale factoring of "FP8 and FP4 inference, SmoothQuant and activation
 // quantization" (Scale granularity) and the epilogue of "FP8 and INT8 Inference" §6-9.
 //
@@ -57,7 +59,7 @@ __device__ __forceinline__ void so_barrier() { asm volatile("s_barrier" ::: "mem
 
 typedef int sfrag_t __attribute__((ext_vector_type(8)));
 
-template <bool OF8>
+template <int KIND, bool OF8>
 __global__ void __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 gemm_solo_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
                  const uint8_t* __restrict__ wq, const float* __restrict__ sw, int M, int N,
@@ -121,11 +123,12 @@ gemm_solo_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
     else { F[f][0] = v[0]; F[f][1] = v[1]; F[f][2] = v[2]; F[f][3] = v[3]; }
   };
 
-  f32x4 acc[SN][SM];
+  typedef typename std::conditional<KIND == 1, i32x4, f32x4>::type acc_t;
+  acc_t acc[SN][SM];
 #pragma unroll
   for (int j = 0; j < SN; ++j)
 #pragma unroll
-    for (int i = 0; i < SM; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < SM; ++i) acc[j][i] = acc_t{};
   sfrag_t F0[NF], F1[NF];
 
   // One K step: MFMAs on `cur` (step s), reads of step s + 1 into `nxt`, loads of step
@@ -139,7 +142,17 @@ gemm_solo_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 #pragma unroll
     for (int tt = 0; tt < T; ++tt) {
       const int i = tt % SM, j = tt / SM;
-      acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur[SM + j], cur[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+      if constexpr (KIND == 1) {
+        // INT8: the fragment's two 16-byte chunks are the two 64-deep halves of the step.
+        const sfrag_t& a = cur[SM + j];
+        const sfrag_t& b = cur[i];
+        acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{a[0], a[1], a[2], a[3]}, i32x4{b[0], b[1], b[2], b[3]},
+                                                         acc[j][i], 0, 0, 0);
+        acc[j][i] = __builtin_amdgcn_mfma_i32_16x16x64_i8(i32x4{a[4], a[5], a[6], a[7]}, i32x4{b[4], b[5], b[6], b[7]},
+                                                         acc[j][i], 0, 0, 0);
+      } else {
+        acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(cur[SM + j], cur[i], acc[j][i], 0, 0, 0, 0, 0, 0);
+      }
       if (tt < 2 * NF) read_half(nxt, stn, tt);
       if ((tt & 1) && (tt >> 1) < L) dma_one(kl, std_, tt >> 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -210,14 +223,15 @@ gemm_solo_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = acc[j][i][r] * (esm[i] * esn[j][r]);
+          if constexpr (KIND == 1) v[r] = mul_rn(mul_rn((float)acc[j][i][r], esm[i]), esn[j][r]);
+          else v[r] = acc[j][i][r] * (esm[i] * esn[j][r]);
           if constexpr (BIAS) v[r] = add_rn(v[r], bf16_lo(ep.bias[min(n0 + cl + r, N - 1)]));
           v[r] = epi_act<ACT>(v[r]);
         }
         if constexpr (OF8) {
           *reinterpret_cast<uint32_t*>(lds + rl * RS + cl) =
-              pack_e4m3x4(epi_requant<false>(v[0], ep.s_out, ep.inv_s_out), epi_requant<false>(v[1], ep.s_out, ep.inv_s_out),
-                          epi_requant<false>(v[2], ep.s_out, ep.inv_s_out), epi_requant<false>(v[3], ep.s_out, ep.inv_s_out));
+              pack_e4m3x4(epi_requant<KIND == 1>(v[0], ep.s_out, ep.inv_s_out), epi_requant<KIND == 1>(v[1], ep.s_out, ep.inv_s_out),
+                          epi_requant<KIND == 1>(v[2], ep.s_out, ep.inv_s_out), epi_requant<KIND == 1>(v[3], ep.s_out, ep.inv_s_out));
         } else {
           const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           *reinterpret_cast<u32x2*>(lds + rl * RS + cl * 2) = o;
@@ -263,19 +277,25 @@ gemm_solo_kernel(const uint8_t* __restrict__ xq, const float* __restrict__ sx,
 }  // namespace
 
 hipError_t launch_gemm_solo(const void* xq, const float* sx, const void* wq, const float* sw,
-                            int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                             const Epilogue& ep) {
   const int tiles_m = (int)((M + kSoloBM - 1) / kSoloBM);
   const int tiles_n = (int)((N + kSoloBN - 1) / kSoloBN);
   const int vec = ep.out_fp8 ? (N % 16) == 0 : (N % 8) == 0;
-  if (ep.out_fp8)
-    hipLaunchKernelGGL((gemm_solo_kernel<true>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kSoloThreads), 0, st,
-                       (const uint8_t*)xq, sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, (int)(K / 128), y,
-                       tiles_m, vec, ep);
-  else
-    hipLaunchKernelGGL((gemm_solo_kernel<false>), dim3((unsigned)(tiles_m * tiles_n)), dim3(kSoloThreads), 0, st,
-                       (const uint8_t*)xq, sx, (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, (int)(K / 128), y,
-                       tiles_m, vec, ep);
+  auto go = [&](auto kind_c, auto of8_c) {
+    hipLaunchKernelGGL((gemm_solo_kernel<decltype(kind_c)::value, decltype(of8_c)::value>),
+                       dim3((unsigned)(tiles_m * tiles_n)), dim3(kSoloThreads), 0, st, (const uint8_t*)xq, sx,
+                       (const uint8_t*)wq, sw, (int)M, (int)N, (int)K, (int)(K / 128), y, tiles_m, vec, ep);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if (fmt == 1) {
+    if (ep.out_fp8) go(I1{}, std::true_type{});
+    else go(I1{}, std::false_type{});
+  } else {
+    if (ep.out_fp8) go(I0{}, std::true_type{});
+    else go(I0{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 

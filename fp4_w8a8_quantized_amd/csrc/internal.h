@@ -34,16 +34,16 @@ struct Epilogue {
 hipError_t launch_gemm(const void* xq, const float* sx, const void* wq, const float* sw,
                        int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                        const Epilogue& ep = Epilogue{});
-// FP8 form of launch_gemm for more tokens than the few-token kernel takes: 8 waves per
+// launch_gemm for more tokens than the narrow tiles take (fmt 0 FP8, 1 INT8): 8 waves per
 // workgroup, two per SIMD alternating between LDS reads and MFMAs.
 hipError_t launch_gemm_pp(const void* xq, const float* sx, const void* wq, const float* sw,
-                          int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                          int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                           const Epilogue& ep);
 
-// FP8 256 x 128 tiles on one wave per SIMD (128 x 64 wave tiles, fragments double-buffered,
-// one barrier per K step).
+// 256 x 128 tiles on one wave per SIMD (128 x 64 wave tiles, fragments double-buffered,
+// one barrier per K step), fmt 0 FP8 or 1 INT8.
 hipError_t launch_gemm_solo(const void* xq, const float* sx, const void* wq, const float* sw,
-                            int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
+                            int64_t M, int64_t N, int64_t K, int fmt, void* y, hipStream_t st,
                             const Epilogue& ep);
 
 // One token where the vector kernel does not take K: weights streamed by 16-row workgroups
@@ -71,10 +71,6 @@ bool use_w4a16_mid(int64_t M, int64_t N, int64_t K);
 bool use_w4a16_gemv(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_w4a16_mid(const void* x, const void* wq, const uint16_t* sc, int64_t M,
                                  int64_t N, int64_t K, void* y, hipStream_t st);
-// INT8 form of the MXFP4 two-waves-per-SIMD kernel (256 x 128 tiles, 32x32x32 MFMAs).
-hipError_t launch_gemm_int8_pp(const void* xq, const float* sx, const void* wq, const float* sw,
-                               int64_t M, int64_t N, int64_t K, void* y, hipStream_t st,
-                               const Epilogue& ep);
 // MXFP4 on 256 x 256 tiles, one wave per SIMD (128 x 128 wave tiles, accumulators in AGPRs).
 hipError_t launch_gemm_mx_solo(const void* xq, const uint8_t* sx, const void* wq, const uint8_t* sw,
                                int64_t M, int64_t N, int64_t K, void* y, hipStream_t st);
