@@ -172,20 +172,4 @@ __device__ __forceinline__ float amax_scale(float amax, float qmax) {
   return a / qmax;                      // IEEE fp32 division
 }
 
-// E2M1 code of an fp32 value: round half to even onto the grid 0, 0.5, 1, 1.5, 2, 3, 4, 6,
-// saturating at 6; bit 3 is the sign (a zero keeps its sign).
-__device__ __forceinline__ uint32_t e2m1_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 28) & 8u;
-  const uint32_t a = u & 0x7FFFFFFFu;
-  uint32_t c;
-  if (a < 0x3F800000u) {                 // |v| < 1: grid step 0.5 -> rint(2|v|) in 0..2
-    c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 2.0f);
-  } else {                               // keep one mantissa bit, half-to-even
-    const uint32_t r = a + 0x1FFFFFu + ((a >> 22) & 1u);
-    c = min((r >> 22) - 252u, 7u);
-  }
-  return sign | c;
-}
-
 }  // namespace w8a8
