@@ -11,17 +11,21 @@
 // GEMM: organised like the few-token FP8 kernel, around streaming W once at HBM rate. A
 // workgroup owns 16 NW weight rows; its WPB waves split the K groups (wave w: groups w,
 // w + WPB, ...). Per group a lane reads 16 bytes of its row (32 codes, K offsets 32 g + 0..31
-// of the group for lane group g = lane >> 4), converts them to bf16 (exact small integers)
-// and feeds four 16x16x32 bf16 MFMAs; X supplies the same K offsets. S is kept outside the
-// group's sum: the group's fp32 partial is multiplied by S[n, group] and accumulated, which
-// keeps every product exact (S q would need up to 14 significant bits). The waves' sums
-// meet in LDS. M above 128 is processed in slices of 128 rows (each re-reads W).
+// of the group for lane group g = lane >> 4), converts them to bf16 pairs of 136 + code with
+// the biased conversion below (seven integer instructions per eight codes; the exact
+// conversion through fp32 took about 28 and measured 2-4% slower) and feeds four 16x16x32
+// bf16 MFMAs; X supplies the same K offsets, re-paired to the codes' pairs, and four more
+// MFMAs against ones give 136 times its sum, which comes off the group's partial. S is kept
+// outside the group's sum: the group's fp32 partial is multiplied by S[n, group] and
+// accumulated, which keeps every product exact (S q would need up to 14 significant bits).
+// The waves' sums meet in LDS. M above 128 is processed in slices of 128 rows (each re-reads
+// W).
 //
 // GEMV (one token, K a multiple of 2048 up to 16384): the weight stream in whole rows. A
 // 16-byte-per-lane load of the tile kernel above covers 16 rows x 64 bytes, half a cache line
 // per row. Here each wave reads whole weight rows, a kilobyte of one row per load (8 full
 // lines); each lane keeps its K / 64 elements of X in registers for the whole kernel,
-// dequantizes its 32 codes per load with the biased conversion below and takes the products
+// dequantizes its 32 codes per load with the biased conversion and takes the products
 // with v_dot2 (two bf16 products accumulated in fp32 per instruction); the row's sum is reduced
 // across the wave with DPP moves. The vector unit's work is a large part of the time on wide
 // layers: the conversion at seven instructions per eight codes (one three-input bitwise op
@@ -75,15 +79,26 @@ __global__ __launch_bounds__(256) void quant_int4_kernel(const u32x4* __restrict
 }
 
 // ------------------------------------------------------------------------------- GEMM
-// Eight 4-bit two's-complement codes (one word, element 2i in the low nibble of byte i) as
-// eight bf16 (exact).
-__device__ __forceinline__ bf16x8 int4x8_to_bf16(uint32_t w) {
-  float f[8];
+// Eight 4-bit two's-complement codes n (one word, element 2i in the low nibble of byte i) as
+// four bf16 pairs of 136 + n, exactly, pair k (k < 4) being (136 + n_k, 136 + n_{k+4}), whose
+// nibbles sit 16 bits apart in the word. With n + 8 = n ^ 8 (the unsigned nibble u), the bf16
+// pattern 0x4300 | u is 128 + u; every product x (136 + n) is exact in fp32, and the bias
+// comes off each sum as 136 sum x. For a nibble c = n mod 16, c ^ 8 = n + 8, so the pair is
+// ((w >> 4k) & 0x000F000F) ^ 0x43084308: one three-input bitwise instruction (v_bitop3_b32)
+// and one shift for k > 0, seven instructions a word. The two masks are handed over in
+// registers (m, kc): as literals they would not fit one instruction. The partner operand pairs
+// x_k with x_{k+4}.
+__device__ __forceinline__ void int4x8_to_bf16_biased_k4(uint32_t w, uint32_t m, uint32_t kc,
+                                                         uint32_t (&p)[4]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = (float)((int)(w << (28 - 4 * e)) >> 28);
-  const uint32_t p0 = pack_bf16x2(f[0], f[1]), p1 = pack_bf16x2(f[2], f[3]);
-  const uint32_t p2 = pack_bf16x2(f[4], f[5]), p3 = pack_bf16x2(f[6], f[7]);
-  return __builtin_bit_cast(bf16x8, u32x4{p0, p1, p2, p3});
+  for (int k = 0; k < 4; ++k) p[k] = ((w >> (4 * k)) & m) ^ kc;
+}
+
+// A constant in a vector register that the compiler cannot fold back into an instruction.
+__device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
+  return r;
 }
 
 template <int MT, int WPB, int NW>
@@ -137,6 +152,8 @@ gemm_w4a16_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq
       for (int q = 0; q < 4; ++q)
         xn[i][q] = *reinterpret_cast<const u32x4*>(xrow[i] + (int64_t)gi * kG + 8 * q);
   };
+  const uint32_t m4 = vreg_const(0x000F000Fu), kc4 = vreg_const(0x43084308u);
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
   if (cnt > 0) load(0);
   for (int s = 0; s < cnt; ++s) {
     u32x4 wc[NW];
@@ -153,20 +170,40 @@ gemm_w4a16_kernel(const uint16_t* __restrict__ x, const uint8_t* __restrict__ wq
 #pragma unroll
       for (int q = 0; q < 4; ++q) xv[i][q] = xn[i][q];
     if (s + 1 < cnt) load(s + 1);
+    // X re-paired to the codes' pairs (x_k, x_{k+4}) of each 8-element word, and 136 times
+    // each token's sum over the group (MFMAs against ones: the same in every output row).
+    u32x4 xp[MT][4];
+    f32x4 xb[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      f32x4 xs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 v = xv[i][q];
+        xp[i][q] = u32x4{__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                         __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u)};
+        xs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, __builtin_bit_cast(bf16x8, v), xs, 0, 0, 0);
+      }
+      xb[i] = xs * 136.0f;
+    }
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       const uint32_t ww[4] = {wc[j].x, wc[j].y, wc[j].z, wc[j].w};
       bf16x8 wf[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wf[q] = int4x8_to_bf16(ww[q]);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t pk[4];
+        int4x8_to_bf16_biased_k4(ww[q], m4, kc4, pk);
+        wf[q] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
         f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[q], __builtin_bit_cast(bf16x8, xv[i][q]), part, 0, 0, 0);
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[q], __builtin_bit_cast(bf16x8, xp[i][q]), part, 0, 0, 0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[r], scur[j][r], acc[j][i][r]);
+        for (int r = 0; r < 4; ++r) acc[j][i][r] = __builtin_fmaf(part[r] - xb[i][r], scur[j][r], acc[j][i][r]);
       }
     }
   }
@@ -218,38 +255,6 @@ hipError_t launch_w4a16_slice(const void* x, const void* wq, const uint16_t* sc,
   return launch_w4a16_cfg<8, 4, 1>(x, wq, sc, M, N, K, y, st);
 }
 
-
-// Eight 4-bit two's-complement codes n (one word, element 2i in the low nibble of byte i) as
-// four bf16 pairs of 136 + n, exactly: n + 8 = n ^ 8 is the unsigned nibble u, and the bf16
-// pattern 0x4300 | u is 128 + u (one unit in the last place at 128). That is 1.5 integer
-// instructions per element (xor, two masks, a byte permute and an or per pair); the bias 136
-// comes off each row's sum as 136 sum_k x_k. Every product x (136 + n) is exact in fp32.
-__device__ __forceinline__ void int4x8_to_bf16_biased(uint32_t w, uint32_t (&p)[4]) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;   // u0 u2 u4 u6 | u1 u3 u5 u7
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    p[i] = __builtin_amdgcn_perm(hi, lo, 0x0C000C00u | ((4u + i) << 16) | (uint32_t)i) | 0x43004300u;
-}
-
-// The same, paired differently: pair k (k < 4) is (136 + n_k, 136 + n_{k+4}), whose nibbles
-// sit 16 bits apart in the word. For a nibble c = n mod 16, c ^ 8 = n + 8, so the pair is
-// ((w >> 4k) & 0x000F000F) ^ 0x43084308: one three-input bitwise instruction (v_bitop3_b32)
-// and one shift for k > 0, seven instructions a word. The two masks are handed over in
-// registers (m, kc): as literals they would not fit one instruction. The partner operand pairs
-// x_k with x_{k+4}.
-__device__ __forceinline__ void int4x8_to_bf16_biased_k4(uint32_t w, uint32_t m, uint32_t kc,
-                                                         uint32_t (&p)[4]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) p[k] = ((w >> (4 * k)) & m) ^ kc;
-}
-
-// A constant in a vector register that the compiler cannot fold back into an instruction.
-__device__ __forceinline__ uint32_t vreg_const(uint32_t c) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(c));
-  return r;
-}
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
