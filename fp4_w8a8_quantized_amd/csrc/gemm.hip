@@ -9,8 +9,8 @@
 // Dispatch by shape:
 //  - one token (K a multiple of 1024 up to 16384): whole weight rows per wave on the vector
 //    unit (gemm_gemv.hip);
-//  - 2-128 tokens, and 129-512 tokens where one round of 128 x 64 or 128 x 128 tiles covers
-//    the output: narrow tiles sized to the token count (gemm_narrow.hip);
+//  - 2-128 tokens, and 129-512 tokens where one round of 64 x 64, 128 x 64 or 128 x 128
+//    tiles covers the output: narrow tiles sized to the token count (gemm_narrow.hip);
 //  - one token that the vector kernel does not take: the weight-streaming split-K kernel
 //    (gemm_skinny.hip);
 //  - otherwise the prefill kernels (gemm_pp.hip, and gemm_solo.hip for 128-wide tiles): FP8

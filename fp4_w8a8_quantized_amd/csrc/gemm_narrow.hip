@@ -349,7 +349,10 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   K = 14336: 16 x 4096 20.4 -> 13.0 us, 32 x 4096 27.2 -> 16.9, 128 x 4096 35.9 -> 26.3,
 //              192 x 4096 48.7 -> 45.9.
 // Wider layers take 64 or 128 weight rows, 128 where 64 would need a second round; above
-// 128 tokens, 128 x 64 or 128 x 128 tiles where one round of them covers the output.
+// 128 tokens, 64 x 64 tiles where one round of them covers the output, else 128 x 64 or
+// 128 x 128. A CU streams its tile's rows at about the same rate whatever the tile, so the
+// tiles that use every CU win: 64 x 64 against 128 x 64 took 256 x 4096 from 15.8 to 11.9 us,
+// 160 x 4096 15.4 -> 10.9, 256 x 2048 15.6 -> 11.3 and 256 x 4096 x 14336 45.5 -> 33.5.
 int narrow_config(int64_t M, int64_t N) {
   if (M < 2 || N < 1) return -1;
   if (M <= 16) {
@@ -373,6 +376,7 @@ int narrow_config(int64_t M, int64_t N) {
     return cdiv(N, 64) <= 256 ? 10 : 11;
   }
   if (M <= 512) {
+    if (cdiv(M, 64) * cdiv(N, 64) <= 256) return 8;
     if (cdiv(M, 128) * cdiv(N, 64) <= 256) return 10;
     if (cdiv(M, 128) * cdiv(N, 128) <= 256) return 11;
   }
