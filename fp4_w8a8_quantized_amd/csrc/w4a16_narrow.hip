@@ -290,12 +290,17 @@ int64_t w4n_cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   65-128 tokens: 32 x 64 where one round covers the output (128 x 4096 20.1 -> 18.9 us).
 // On wider layers above 32 tokens the LDS-staged kernel stays faster (64 x 14336: 30.4
 // against 36.7 us here).
-// Up to 16 tokens on narrower layers the decode kernel stays faster (8 x 4096: 6.3 against
-// 7.2 us): its 8 waves per workgroup hide the load latency that this kernel's stages expose.
+//   2-16 tokens on 4097-8192 outputs: 16 x 16 (K split over the 4 waves; 8 staged X rows
+//     up to 8 tokens): 8 x 8192 10.4 -> 8.7 us, 16 x 8192 12.7 -> 9.6.
+// Up to 16 tokens on narrower layers the decode kernel stays faster (8 x 4096: 6.1 against
+// 7.0 us): its 8 waves per workgroup hide the load latency that this kernel's stages expose.
 int w4a16_narrow_config(int64_t M, int64_t N, int64_t K) {
   if (M < 2 || M > 128 || N < 1 || K % 512 != 0) return -1;
-  if (M <= 8) return (N > 8192 && w4n_cdiv(N, 32) <= 512) ? 4 : -1;
-  if (M <= 16) return (N > 8192 && w4n_cdiv(N, 32) <= 512) ? 1 : -1;
+  if (M <= 16) {
+    if (N > 8192) return w4n_cdiv(N, 32) <= 512 ? (M <= 8 ? 4 : 1) : -1;
+    if (N > 4096) return M <= 8 ? 5 : 0;
+    return -1;
+  }
   if (M <= 32) {
     if (2 * w4n_cdiv(N, 16) <= 512) return 0;
     if (2 * w4n_cdiv(N, 32) <= 512) return 1;
@@ -314,6 +319,7 @@ hipError_t launch_gemm_w4a16_narrow(const void* x, const void* wq, const uint16_
     case 1: return launch_w4n<16, 32, 2, 3>(x, wq, sc, M, N, K, y, st);
     case 2: return launch_w4n<32, 64, 1, 3>(x, wq, sc, M, N, K, y, st);
     case 4: return launch_w4n<16, 32, 2, 3, 8>(x, wq, sc, M, N, K, y, st);
+    case 5: return launch_w4n<16, 16, 4, 3, 8>(x, wq, sc, M, N, K, y, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -101,14 +101,16 @@ def test_gemm_w4a16_gemv(M, N, K):
 
 # 2-128 tokens with K a multiple of 512 take the narrow-tile kernel where one round of tiles
 # covers the output: 16 x 32 tiles (2-16 tokens above 8192 outputs, with 8 staged rows of X up
-# to 8 tokens; 17-32 up to 8192; 33-64 up to 4096), 16 x 16 tiles (17-32 tokens up to 4096
-# outputs, groups split over 4 waves) and 32 x 64 tiles (17-32 tokens up to 16384; 65-128 up to
+# to 8 tokens; 17-32 up to 8192; 33-64 up to 4096), 16 x 16 tiles (2-16 tokens on 4097-8192
+# outputs, 8 staged rows of X up to 8 tokens; 17-32 tokens up to 4096 outputs; groups split
+# over 4 waves) and 32 x 64 tiles (17-32 tokens up to 16384; 65-128 up to
 # 4096); ragged M and N, one stage (K = 512, fewer stages than the ring holds) up to many
 @pytest.mark.parametrize("M,N,K", [(2, 8193, 512), (5, 9000, 1536), (8, 14336, 4096), (7, 16000, 2048),
                                    (9, 8200, 512), (12, 9001, 2048), (16, 16384, 1536), (17, 100, 512),
                                    (20, 4099, 1536), (32, 4096, 4096), (24, 6144, 1024), (31, 8191, 512),
                                    (25, 9000, 1536), (32, 14336, 2048), (33, 4096, 512), (64, 4090, 1536),
-                                   (50, 300, 4096), (65, 4096, 1024), (128, 4100, 512), (100, 2000, 2048)])
+                                   (50, 300, 4096), (65, 4096, 1024), (128, 4100, 512), (100, 2000, 2048),
+                                   (2, 4097, 512), (5, 6144, 1536), (8, 8192, 4096), (12, 8000, 1024), (16, 5000, 2048)])
 def test_gemm_w4a16_narrow(M, N, K):
     need_gpu()
     rng = np.random.default_rng(M * 11 + N * 7 + K)
