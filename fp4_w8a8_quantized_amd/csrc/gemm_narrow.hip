@@ -308,6 +308,7 @@ hipError_t launch_nw(const void* xq, const float* sx, const void* wq, const floa
 //   2  16 x 64,  4 waves, 256 x 4                                 [80 KB]
 //   3  32 x 64,  4 waves, 512 x 3                                 [144 KB]
 //   4-7  (16 | 32) x (64 | 128) on 128-byte steps, 4 waves
+//   12  96 x 64, 8 waves, 256 x 3                                [120 KB]
 //   8-11 (64 | 128) x (64 | 128), 8 waves: 8 waves issue twice the loads at once, which
 //     measured 5-13% faster than 4 on these tiles (512 x 4096 18.4 -> 16.7 us, 48 x 14336
 //     16.4 -> 14.9, 384 x 4096 x 14336 52.0 -> 46.4, 100 x 20000 29.0 -> 25.3); on the
@@ -328,6 +329,7 @@ hipError_t launch_nw_cfg(int c, const void* xq, const float* sx, const void* wq,
     case 9: return launch_nw<KIND, 64, 128, 1, 128, 4, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
     case 10: return launch_nw<KIND, 128, 64, 1, 256, 3, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
     case 11: return launch_nw<KIND, 128, 128, 1, 128, 4, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
+    case 12: return launch_nw<KIND, 96, 64, 1, 256, 3, 8>(xq, sx, wq, sw, M, N, K, y, st, ep);
     default: return hipErrorInvalidValue;
   }
 }
@@ -349,10 +351,12 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   K = 14336: 16 x 4096 20.4 -> 13.0 us, 32 x 4096 27.2 -> 16.9, 128 x 4096 35.9 -> 26.3,
 //              192 x 4096 48.7 -> 45.9.
 // Wider layers take 64 or 128 weight rows, 128 where 64 would need a second round; above
-// 128 tokens, 64 x 64 tiles where one round of them covers the output, else 128 x 64 or
-// 128 x 128. A CU streams its tile's rows at about the same rate whatever the tile, so the
-// tiles that use every CU win: 64 x 64 against 128 x 64 took 256 x 4096 from 15.8 to 11.9 us,
-// 160 x 4096 15.4 -> 10.9, 256 x 2048 15.6 -> 11.3 and 256 x 4096 x 14336 45.5 -> 33.5.
+// 128 tokens, 64 x 64 tiles where one round of them covers the output, else 96 x 64, else
+// 128 x 64 or 128 x 128. A CU streams its tile's rows at about the same rate whatever the
+// tile, so the smallest tiles that fit one round win: 64 x 64 against 128 x 64 took
+// 256 x 4096 from 15.8 to 11.9 us, 160 x 4096 15.4 -> 10.9, 256 x 2048 15.6 -> 11.3 and
+// 256 x 4096 x 14336 45.5 -> 33.5; 96 x 64 against 128 x 64 took 384 x 4096 15.9 -> 13.7,
+// 300 x 4096 15.6 -> 13.2 and 384 x 4096 x 14336 45.5 -> 39.0.
 int narrow_config(int64_t M, int64_t N) {
   if (M < 2 || N < 1) return -1;
   if (M <= 16) {
@@ -377,6 +381,7 @@ int narrow_config(int64_t M, int64_t N) {
   }
   if (M <= 512) {
     if (cdiv(M, 64) * cdiv(N, 64) <= 256) return 8;
+    if (cdiv(M, 96) * cdiv(N, 64) <= 256) return 12;
     if (cdiv(M, 128) * cdiv(N, 64) <= 256) return 10;
     if (cdiv(M, 128) * cdiv(N, 128) <= 256) return 11;
   }

@@ -53,7 +53,7 @@ def _check(y, o, fmt, what):
 # 16 x 64 and 32 x 64 on 256- and 512-byte stages, the 128-byte-step tiles (16 / 32 token
 # rows x 64 / 128 weight rows), and the 8-wave 64 x 64, 64 x 128, 128 x 64 and 128 x 128
 # tiles (64 x 64: 65-128 tokens on 4097-8192 outputs and 129-256 tokens up to 4096 outputs;
-# 128 x 64 and 128 x 128: 129-512 tokens); ragged M and N (N not a multiple of 4 or 16);
+# 96 x 64: 257-384 tokens up to 4096 outputs; 128 x 64 and 128 x 128: 129-512 tokens); ragged M and N (N not a multiple of 4 or 16);
 # K a whole number of stages, and K ending in a partial stage (fewer K steps than a stage
 # holds: one, or fewer than the waves splitting it), including K shorter than one stage;
 # step counts below and above the ring depth; several row tiles (257-512 tokens); K = 14336.
@@ -64,7 +64,8 @@ CASES = [(1, 6144, 4096), (5, 4096, 4096), (16, 1000, 640), (9, 3000, 896), (12,
          (128, 14336, 1024), (100, 20000, 256), (128, 28672, 128), (256, 4096, 384), (300, 4101, 256),
          (512, 4096, 1152), (257, 6144, 128), (384, 4096, 14336), (16, 4096, 14336), (128, 4096, 14336),
          (100, 6144, 896), (80, 8192, 4096), (129, 4100, 640), (200, 6144, 1152), (255, 9000, 512),
-         (384, 6144, 640), (511, 8190, 256), (250, 4000, 1408), (192, 2048, 4096)]
+         (384, 6144, 640), (511, 8190, 256), (250, 4000, 1408), (192, 2048, 4096),
+         (300, 4096, 1152), (350, 3000, 896)]
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
