@@ -9,7 +9,7 @@
 // Dispatch by shape:
 //  - one token (K a multiple of 1024 up to 16384): whole weight rows per wave on the vector
 //    unit (gemm_gemv.hip);
-//  - 2-128 tokens, and 129-512 tokens where one round of 64 x 64, 96 x 64, 128 x 64 or 128 x 128
+//  - 2-128 tokens, and more tokens where one round of 64 x 64, 96 x 64, 128 x 64 or 128 x 128
 //    tiles covers the output: narrow tiles sized to the token count (gemm_narrow.hip);
 //  - one token that the vector kernel does not take: the weight-streaming split-K kernel
 //    (gemm_skinny.hip);

@@ -356,7 +356,11 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // tile, so the smallest tiles that fit one round win: 64 x 64 against 128 x 64 took
 // 256 x 4096 from 15.8 to 11.9 us, 160 x 4096 15.4 -> 10.9, 256 x 2048 15.6 -> 11.3 and
 // 256 x 4096 x 14336 45.5 -> 33.5; 96 x 64 against 128 x 64 took 384 x 4096 15.9 -> 13.7,
-// 300 x 4096 15.6 -> 13.2 and 384 x 4096 x 14336 45.5 -> 39.0.
+// 300 x 4096 15.6 -> 13.2 and 384 x 4096 x 14336 45.5 -> 39.0. The same holds at any token
+// count: where one round of these tiles covers the output, the prefill kernels' 256-row tiles
+// fill at most half the CUs, and the narrow tiles won on every such shape measured (1024 x 4096
+// 29.1 -> 23.0 us, 1024 x 2048 28.6 -> 16.2, 2048 x 2048 28.0 -> 23.1, 900 x 1024 25.7 -> 10.7,
+// 8192 x 512 28.0 -> 25.1, 1024 x 4096 x 14336 85.8 -> 68.4, 2048 x 1024 x 14336 81.6 -> 47.2).
 int narrow_config(int64_t M, int64_t N) {
   if (M < 2 || N < 1) return -1;
   if (M <= 16) {
@@ -379,12 +383,10 @@ int narrow_config(int64_t M, int64_t N) {
     if (2 * cdiv(N, 64) <= 256) return 8;
     return cdiv(N, 64) <= 256 ? 10 : 11;
   }
-  if (M <= 512) {
-    if (cdiv(M, 64) * cdiv(N, 64) <= 256) return 8;
-    if (cdiv(M, 96) * cdiv(N, 64) <= 256) return 12;
-    if (cdiv(M, 128) * cdiv(N, 64) <= 256) return 10;
-    if (cdiv(M, 128) * cdiv(N, 128) <= 256) return 11;
-  }
+  if (cdiv(M, 64) * cdiv(N, 64) <= 256) return 8;
+  if (cdiv(M, 96) * cdiv(N, 64) <= 256) return 12;
+  if (cdiv(M, 128) * cdiv(N, 64) <= 256) return 10;
+  if (cdiv(M, 128) * cdiv(N, 128) <= 256) return 11;
   return -1;
 }
 

@@ -86,7 +86,7 @@ hipError_t launch_smooth_apply(const void* x, int64_t R, int64_t K, const float*
                                void* out, hipStream_t st);
 
 // Narrow output tiles sized to the token count (16-128 token rows x 16-128 weight rows, 4 or
-// 8 waves, K through an LDS ring of row-contiguous stages): 2-128 tokens, and 129-512 tokens
+// 8 waves, K through an LDS ring of row-contiguous stages): 2-128 tokens, and more tokens
 // where one round of 64 x 64, 96 x 64, 128 x 64 or 128 x 128 tiles covers the output (use_gemm_narrow).
 bool use_gemm_narrow(int64_t M, int64_t N, int64_t K);
 // W4A16, 9-128 tokens with K a multiple of 512 where one round of its tiles covers the output

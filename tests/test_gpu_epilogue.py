@@ -22,10 +22,10 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-2
 
 # the prefill kernels (ragged and 16-aligned N), every narrow tile (16 x 16 with K split over
-# 4 waves, 16 x 32, 16 x 64, 32 x 64, and the 8-wave 64- and 128-row tiles at 65-512 tokens,
+# 4 waves, 16 x 32, 16 x 64, 32 x 64, and the 8-wave 64-, 96- and 128-row tiles above 64 tokens,
 # one and several row tiles) and the one-token vector kernel (its epilogue runs in one lane
 # per output)
-SHAPES = [(600, 549, 256), (256, 512, 384), (5, 130, 1152), (64, 10000, 256), (100, 262, 512),
+SHAPES = [(1100, 4100, 256), (2048, 4096, 128), (600, 549, 256), (256, 512, 384), (5, 130, 1152), (64, 10000, 256), (100, 262, 512),
           (128, 9001, 256), (200, 9001, 384), (300, 549, 256), (448, 2050, 256),
           (300, 6100, 384), (100, 20001, 256), (48, 40000, 128), (40, 4100, 256),
           (16, 6144, 512), (300, 4096, 384), (1, 4100, 2048), (1, 77, 14336)]

@@ -59,25 +59,26 @@ def test_fp8_tiny_config():
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 256), (3, 1000, 4096),
-                                   (256, 256, 128), (513, 129, 1024), (260, 4100, 256)])
+                                   (256, 256, 128), (513, 129, 1024), (260, 4100, 256), (1100, 4100, 512)])
 def test_fp8_ragged(M, N, K):
     need_gpu()
     xb, wb = _xw(M, N, K, M * 31 + N * 7 + K)
     _fp8_full_compare(xb, wb, f"{M}x{N}x{K}")
 
 
-# Few-token and mid-size paths (2-512 tokens, the narrow-tile kernel): every tile and several
-# row tiles, every 16-row bucket edge, N not a multiple of 4 or 16, one K step and K ending in
-# a partial stage, step counts below and above the ring depth, wide layers with a ragged last
-# tile (up to 128 weight rows per tile), and the prefill kernels where narrow tiles would take
-# more than one round of the CUs (513 tokens, 200 tokens on 20000 outputs, 400 on 7000).
+# Few-token and mid-size paths (the narrow-tile kernel): every tile and several row tiles,
+# every 16-row bucket edge, N not a multiple of 4 or 16, one K step and K ending in a partial
+# stage, step counts below and above the ring depth, wide layers with a ragged last tile (up
+# to 128 weight rows per tile), 513 tokens on 1000 outputs, and the prefill kernels where
+# narrow tiles would take more than one round of the CUs (200 tokens on 20000 outputs, 400 on
+# 7000, 1100 on 4100).
 FEW_TOKEN_CASES = [(16, 33, 1152), (32, 7, 128), (33, 64, 640), (64, 4099, 256), (65, 100, 2048),
                 (128, 130, 1152), (129, 257, 256), (2, 18, 14336), (16, 9000, 256),
                 (32, 8200, 384), (64, 10000, 1152), (128, 8193, 640), (97, 8209, 128),
                 (111, 4097, 2176), (128, 14336, 384), (200, 4100, 640), (256, 9000, 1152),
                 (160, 6144, 512), (257, 300, 256), (100, 20000, 256), (400, 7000, 384),
                 (90, 16500, 384), (128, 32768, 256), (128, 32769, 128), (200, 20000, 256),
-                (513, 1000, 256), (40, 4100, 512), (64, 40000, 256), (48, 33000, 128)]
+                (513, 1000, 256), (1100, 4100, 256), (40, 4100, 512), (64, 40000, 256), (48, 33000, 128)]
 
 
 # One token with K a multiple of 1024 up to 16384 takes the whole-row vector kernel: one to
@@ -212,7 +213,7 @@ def _int8_chain(xb, xcal, wb, alpha, what):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (17, 130, 384), (300, 549, 1024), (64, 256, 14336),
-                                   (513, 129, 1024), (260, 4100, 256), (2049, 1000, 512),
+                                   (513, 129, 1024), (260, 4100, 256), (2049, 1000, 512), (2049, 3000, 512),
                                    (1999, 6001, 384), (2048, 6144, 256)])
 def test_int8_ragged(M, N, K):
     need_gpu()

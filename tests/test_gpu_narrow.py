@@ -1,5 +1,5 @@
-"""GPU parity of the narrow-tile GEMM (the kernel w8a8_gemm uses for 2-512 tokens wherever one
-round of its tiles covers the output) against
+"""GPU parity of the narrow-tile GEMM (the kernel w8a8_gemm uses for two or more tokens wherever
+one round of its tiles covers the output) against
 the oracle: FP8 outputs within |y - y_ref| <= 1e-2 (|y_ref| + rms(y_ref)) of the oracle's fp64
 contraction over the same codes, INT8 outputs bit for bit, repeated launches bit-identical;
 and the shader-clock probe used by the measurements."""
@@ -51,9 +51,9 @@ def _check(y, o, fmt, what):
 
 # Every tile the kernel has: 16 x 16 (4-way K split over the waves), 16 x 32 (2-way),
 # 16 x 64 and 32 x 64 on 256- and 512-byte stages, the 128-byte-step tiles (16 / 32 token
-# rows x 64 / 128 weight rows), and the 8-wave 64 x 64, 64 x 128, 128 x 64 and 128 x 128
-# tiles (64 x 64: 65-128 tokens on 4097-8192 outputs and 129-256 tokens up to 4096 outputs;
-# 96 x 64: 257-384 tokens up to 4096 outputs; 128 x 64 and 128 x 128: 129-512 tokens); ragged M and N (N not a multiple of 4 or 16);
+# rows x 64 / 128 weight rows), and the 8-wave 64 x 64, 64 x 128, 96 x 64, 128 x 64 and
+# 128 x 128 tiles (above 128 tokens the smallest that fits one round of the CUs, at any token
+# count: up to 4100 tokens on 200 outputs); ragged M and N (N not a multiple of 4 or 16);
 # K a whole number of stages, and K ending in a partial stage (fewer K steps than a stage
 # holds: one, or fewer than the waves splitting it), including K shorter than one stage;
 # step counts below and above the ring depth; several row tiles (257-512 tokens); K = 14336.
@@ -65,7 +65,8 @@ CASES = [(1, 6144, 4096), (5, 4096, 4096), (16, 1000, 640), (9, 3000, 896), (12,
          (512, 4096, 1152), (257, 6144, 128), (384, 4096, 14336), (16, 4096, 14336), (128, 4096, 14336),
          (100, 6144, 896), (80, 8192, 4096), (129, 4100, 640), (200, 6144, 1152), (255, 9000, 512),
          (384, 6144, 640), (511, 8190, 256), (250, 4000, 1408), (192, 2048, 4096),
-         (300, 4096, 1152), (350, 3000, 896)]
+         (300, 4096, 1152), (350, 3000, 896),
+         (700, 1000, 640), (1030, 3000, 512), (2048, 1024, 256), (4100, 200, 384)]
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "int8"])
